@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Routed history attention benchmark on one MI355X.
+
+One step = one routed attention call of one layer at the chunk-48 shape
+(40 heads, d = 128, bf16, 36 query blocks, 1692 history blocks, 60% of the
+query blocks geometry-covered): block importance -> route selection -> sparse
+attention, with q/k/v and the key-mean cache resident in HBM. The dense
+attention of the same tensors is timed separately for the speedup.
+
+Prints ONE JSON line on stdout (diagnostics go to stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed attention latency/call (ms) + eff. TFLOP/s % MFMA peak at chunk-48 shape"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dense-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24,
+                    help="query-block rows of the oracle's attention sample")
+    return ap.parse_args()
+
+
+def unique_tile_count(ids, lens, N, M):
+    """Distinct (head, tile) pairs the sparse kernel reads (routed + current chunk)."""
+    import numpy as np
+    ids, lens = ids.cpu().numpy(), lens.cpu().numpy()
+    total = 0
+    for h in range(ids.shape[0]):
+        seen = np.zeros(M, dtype=bool)
+        for i in range(ids.shape[1]):
+            seen[ids[h, i, : lens[h, i]]] = True
+        total += int(seen.sum()) + N
+    return total
+
+
+def cpu_baseline(wl, q, k, v, p, ids, lens, rows_n):
+    """Oracle timed on a bounded sample, extrapolated to one whole call."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    heads = [0, 1]
+    qn = q[heads].float().cpu().numpy()
+    kn = k[heads].float().cpu().numpy()
+    vn = v[heads].float().cpu().numpy()
+    p_np = p[heads].cpu().numpy()
+    ids_np, lens_np = ids.cpu().numpy(), lens.cpu().numpy()
+
+    t0 = time.perf_counter()
+    qb = oracle.block_means(qn[:1])
+    kb = oracle.block_means(kn[:1, : wl.M * 128])
+    oracle.importance(qb, kb, wl.scale)
+    t_imp = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    for i in range(wl.N):
+        oracle.route_row(p_np[0, i], wl.g[i], wl.rho[i], wl.params, wl.M, wl.coords, i)
+    t_route = time.perf_counter() - t0
+
+    rows = [(int(rng.integers(0, 2)), int(rng.integers(0, wl.N))) for _ in range(rows_n)]
+    t0 = time.perf_counter()
+    for h, i in rows:
+        route = ids_np[heads[h], i, : lens_np[heads[h], i]].tolist()
+        oracle.sparse_attention_block(qn, kn, vn, wl.scale, h, i, route, wl.M, wl.N)
+    t_attn = time.perf_counter() - t0
+    n_rows = wl.H * wl.N
+    total_s = wl.H * t_imp + wl.H * t_route + n_rows / rows_n * t_attn
+    return {
+        "value": round(total_s * 1e3, 1),
+        "unit": "ms",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"importance of 1 head, routes of the 36 rows of 1 head, sparse attention of "
+                   f"{rows_n} random (head, block) rows; scaled to 40 heads x 36 rows "
+                   f"(measured {t_imp + t_route + t_attn:.1f} s of CPU time)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; multi-GPU sharding is a design note only)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import geometry_routed_block_amd as velox
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = synth.chunk48()
+    log(f"workload {wl.name}: H={wl.H} d={wl.d} N={wl.N} M={wl.M} {wl.dtype}")
+    q, k, v = synth.make_qkv(wl, device=dev)
+    kbar = velox.block_mean(k[:, : wl.M * 128])
+    g = torch.from_numpy(wl.g).to(dev)
+    rho = torch.from_numpy(wl.rho).to(dev)
+    coord = torch.from_numpy(np.ascontiguousarray(wl.coords, np.int32)).to(dev)
+    L = velox.route_bound(wl.params, wl.M)
+    p = torch.empty(wl.H, wl.N, wl.M, dtype=torch.float32, device=dev)
+    ids = torch.empty(wl.H, wl.N, L, dtype=torch.int32, device=dev)
+    lens = torch.empty(wl.H, wl.N, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step():
+        velox.route_scores(q, kbar, wl.M, out=p)
+        velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
+        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        e = evs[s]
+        e[0].record()
+        velox.route_scores(q, kbar, wl.M, out=p)
+        e[1].record()
+        velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
+        e[2].record()
+        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o)
+        e[3].record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / K
+    t_scores = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_select = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_sparse = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    log(f"timed {K} steps: {ms_per_step:.3f} ms/step (scores {t_scores:.3f}, select {t_select:.3f}, "
+        f"sparse {t_sparse:.3f})")
+
+    # dense baseline on the same tensors
+    od = torch.empty_like(q)
+    velox.dense_attn(q, k, v, wl.M, out=od)
+    torch.cuda.synchronize()
+    ds, de = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ds.record()
+    for _ in range(args.dense_steps):
+        velox.dense_attn(q, k, v, wl.M, out=od)
+    de.record()
+    torch.cuda.synchronize()
+    dense_ms = ds.elapsed_time(de) / args.dense_steps
+
+    lens_np = lens.cpu().numpy()
+    tiles = int((lens_np + wl.N).sum())
+    blk = 128
+    flop = 4.0 * blk * blk * wl.d * tiles
+    flop_hist = 4.0 * blk * blk * wl.d * int(lens_np.sum())
+    dense_flop = 4.0 * blk * blk * wl.d * wl.H * wl.N * (wl.M + wl.N)
+    uniq = unique_tile_count(ids, lens, wl.N, wl.M)
+    tile_bytes = 2 * blk * wl.d * 2                 # K + V of one tile, bf16
+    qo_bytes = 2 * q.numel() * 2
+    uniq_bytes = uniq * tile_bytes + qo_bytes
+    eff_tflops = flop / (ms_per_step * 1e-3) / 1e12
+    kern_tflops = flop / (t_sparse * 1e-3) / 1e12
+    log(f"sparse kernel {kern_tflops:.1f} TFLOP/s ({100 * kern_tflops / PEAK_BF16_TFLOPS:.1f}% of "
+        f"bf16 peak); dense {dense_ms:.3f} ms = {dense_flop / dense_ms / 1e9:.1f} TFLOP/s; "
+        f"speedup {dense_ms / ms_per_step:.2f}x")
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded q/k/v with per-block mean offsets; slab-OBB overlaps)",
+        "config": {
+            "workload": (f"chunk-48 routed attention: H={wl.H}, d={wl.d}, N={wl.N} query blocks, "
+                         f"M={wl.M} history blocks, bf16, 60% covered, K_cov=80, K_unc=150, "
+                         f"n_prev=36, 26-neighbour safeguards"),
+            "global_batch": 1,
+            "seq_len": (wl.M + wl.N) * blk,
+        },
+        "eff_tflops": round(eff_tflops, 1),
+        "pct_mfma_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
+        "breakdown_ms": {"route_scores": round(t_scores, 4), "route_select": round(t_select, 4),
+                         "sparse_attn": round(t_sparse, 4)},
+        "dense_ms": round(dense_ms, 4),
+        "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
+        "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
+        "tiles_visited": tiles,
+        "history_flop_share": round(flop_hist / flop, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(kern_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_bf16_kernel<128, routed>",
+            "hbm_unique_bytes": uniq_bytes,
+            "hbm_frac_unique": round(uniq_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, p, ids, lens, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

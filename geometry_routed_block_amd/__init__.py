@@ -1,0 +1,203 @@
+"""Routed block-sparse history attention for MI355X (gfx950).
+
+Thin PyTorch binding of libvelox.so: every function here only checks tensor
+metadata, marshals pointers and the current HIP stream, and calls the C ABI of
+include/velox.h. All computation runs in the library's HIP kernels.
+
+Layouts (row-major, token rows contiguous):
+    q            [H][N*128][d]          bf16 or fp32
+    k, v         [H][>=(M+N)*128][d]    history blocks 0..M-1, current chunk M..M+N-1
+    kbar         [H][>=M][d]            fp32 key-mean cache
+    p            [H][N][M]              fp32 importance
+    g            [N][M] fp32, rho [N] fp32, coord [M+N][3] int32
+    route_ids    [H][N][L] int32, route_len [H][N] int32
+    o            [H][N*128][d]          dtype of q;  lse [H][N*128] fp32
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+from ._lib import VELOX_BLOCK, VeloxError
+
+__all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
+           "route_bound", "sparse_attn", "dense_attn", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.VELOX_BF16
+    if t.dtype == torch.float32:
+        return _lib.VELOX_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _rows(t, name):
+    """Head stride of a [H][T][d] tensor whose token rows are contiguous."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [H][T][d] with contiguous token rows")
+    return t.stride(0)
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def block_mean(x, nblk: int | None = None, out=None):
+    """Per-block token means (fp32): xbar[h][b] = mean of x[h][128 b : 128 b + 128]."""
+    torch = _torch()
+    _require_cuda(x)
+    H, T, d = x.shape
+    nblk = T // VELOX_BLOCK if nblk is None else nblk
+    if out is None:
+        out = torch.empty(H, nblk, d, dtype=torch.float32, device=x.device)
+    _require_cuda(out)
+    _rows(out.view(H, nblk, d) if out.dim() == 3 else out, "out")
+    lib = _lib.load()
+    _lib.check(lib.velox_block_mean(x.data_ptr(), _dtype_code(x), _rows(x, "x"), H, nblk, d,
+                                    out.data_ptr(), out.stride(0), _stream(x)))
+    return out
+
+
+def route_scores(q, kbar, M: int, scale: float | None = None, out=None):
+    """Block importance p [H][N][M] = softmax over history of scale * qbar . kbar."""
+    torch = _torch()
+    _require_cuda(q, kbar)
+    H, NT, d = q.shape
+    N = NT // VELOX_BLOCK
+    if kbar.dtype != torch.float32:
+        raise TypeError("kbar must be float32")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty(H, N, M, dtype=torch.float32, device=q.device)
+    _require_cuda(out)
+    _contig(out, "p")
+    lib = _lib.load()
+    _lib.check(lib.velox_route_scores(q.data_ptr(), _dtype_code(q), _rows(q, "q"), kbar.data_ptr(),
+                                      _rows(kbar, "kbar"), H, N, M, d, ctypes.c_float(scale),
+                                      out.data_ptr(), _stream(q)))
+    return out
+
+
+def route_bound(params, M: int) -> int:
+    """Smallest route length L that always suffices."""
+    kmax = max(int(params.K_cov), int(params.K_unc), int(params.n_prev))
+    bound = kmax + 26 * int(params.neigh26) + len(tuple(params.ref_ids))
+    return max(1, min(M, bound))
+
+
+def route_select(p, g, rho, coord, params, L: int | None = None, route_ids=None,
+                 route_len=None):
+    """Routes (route_ids [H][N][L] int32, route_len [H][N] int32).
+
+    `params` is any object with the attributes tau, g_ref, lam, eta_cov,
+    theta_cov, theta_unc, K_cov, K_unc, n_prev, neigh26 and ref_ids (a sequence
+    of history ids).
+    """
+    torch = _torch()
+    _require_cuda(p, g, rho)
+    H, N, M = p.shape
+    for t, name in ((p, "p"), (g, "g"), (rho, "rho")):
+        _contig(t, name)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if coord is not None:
+        _require_cuda(coord)
+        _contig(coord, "coord")
+        if coord.dtype != torch.int32:
+            raise TypeError("coord must be int32")
+    L = route_bound(params, M) if L is None else L
+    if route_ids is None:
+        route_ids = torch.empty(H, N, L, dtype=torch.int32, device=p.device)
+    if route_len is None:
+        route_len = torch.empty(H, N, dtype=torch.int32, device=p.device)
+    ref = tuple(int(r) for r in params.ref_ids)
+    ref_t = torch.tensor(ref, dtype=torch.int32, device=p.device) if ref else None
+    c = _lib.RouteParamsC(params.tau, params.g_ref, params.lam, params.eta_cov, params.theta_cov,
+                          params.theta_unc, int(params.K_cov), int(params.K_unc),
+                          int(params.n_prev), int(params.neigh26),
+                          ref_t.data_ptr() if ref_t is not None else None, len(ref))
+    lib = _lib.load()
+    _lib.check(lib.velox_route_select(p.data_ptr(), g.data_ptr(), rho.data_ptr(),
+                                      coord.data_ptr() if coord is not None else None, H, N, M,
+                                      ctypes.byref(c), L, route_ids.data_ptr(),
+                                      route_len.data_ptr(), _stream(p)))
+    if ref_t is not None:
+        ref_t.record_stream(torch.cuda.current_stream(p.device))
+    return route_ids, route_len
+
+
+def _attn_out(q, out, lse, want_lse):
+    torch = _torch()
+    H, NT, d = q.shape
+    if out is None:
+        out = torch.empty(H, NT, d, dtype=q.dtype, device=q.device)
+    _contig(out, "out")
+    if lse is None and want_lse:
+        lse = torch.empty(H, NT, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _contig(lse, "lse")
+    return out, lse
+
+
+def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = True,
+                scale: float | None = None, out=None, lse=None, want_lse: bool = False):
+    """Attention of each query block over its routed history tiles (+ current chunk)."""
+    _require_cuda(q, k, v, route_ids, route_len)
+    H, NT, d = q.shape
+    N = NT // VELOX_BLOCK
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.stride() != v.stride():
+        raise ValueError("q, k, v must share a dtype and k, v a layout")
+    _contig(route_ids, "route_ids")
+    _contig(route_len, "route_len")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out, lse = _attn_out(q, out, lse, want_lse)
+    lib = _lib.load()
+    _lib.check(lib.velox_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                     _rows(q, "q"), _rows(k, "k"), H, N, M, d,
+                                     ctypes.c_float(scale), route_ids.data_ptr(),
+                                     route_len.data_ptr(), route_ids.shape[-1],
+                                     1 if include_current else 0, out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None, _stream(q)))
+    return (out, lse) if want_lse or lse is not None else out
+
+
+def dense_attn(q, k, v, M: int, scale: float | None = None, out=None, lse=None,
+               want_lse: bool = False):
+    """Dense baseline: every history tile and every current-chunk tile."""
+    _require_cuda(q, k, v)
+    H, NT, d = q.shape
+    N = NT // VELOX_BLOCK
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.stride() != v.stride():
+        raise ValueError("q, k, v must share a dtype and k, v a layout")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out, lse = _attn_out(q, out, lse, want_lse)
+    lib = _lib.load()
+    _lib.check(lib.velox_dense_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                    _rows(q, "q"), _rows(k, "k"), H, N, M, d,
+                                    ctypes.c_float(scale), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, _stream(q)))
+    return (out, lse) if want_lse or lse is not None else out

@@ -1,0 +1,170 @@
+// C ABI of libvelox: argument validation, error reporting and dispatch to the
+// kernel launchers. Declarations, layouts and the cited definitions of each
+// operation are in include/velox.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/velox.h"
+#include "velox_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+velox_status_t fail(velox_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+velox_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(VELOX_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return VELOX_OK;
+}
+
+bool dtype_ok(velox_dtype_t dt) { return dt == VELOX_F32 || dt == VELOX_BF16; }
+bool dim_ok(int d) { return d == 64 || d == 128; }
+
+#define REQUIRE(cond, ...)                                    \
+  do {                                                        \
+    if (!(cond)) return fail(VELOX_ERR_INVALID, __VA_ARGS__); \
+  } while (0)
+
+velox_status_t check_common(velox_dtype_t dt, int H, int N, int M, int d) {
+  REQUIRE(dtype_ok(dt), "dtype must be VELOX_F32 or VELOX_BF16 (got %d)", static_cast<int>(dt));
+  REQUIRE(dim_ok(d), "d must be 64 or 128 (got %d)", d);
+  REQUIRE(H >= 1 && N >= 1, "H and N must be >= 1 (got H=%d N=%d)", H, N);
+  REQUIRE(M >= 0, "M must be >= 0 (got %d)", M);
+  if (M > VELOX_MAX_HISTORY)
+    return fail(VELOX_ERR_UNSUPPORTED, "M=%d exceeds VELOX_MAX_HISTORY=%d", M, VELOX_MAX_HISTORY);
+  return VELOX_OK;
+}
+
+velox_status_t check_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                          int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                          float scale, const void* o) {
+  velox_status_t st = check_common(dt, H, N, M, d);
+  if (st != VELOX_OK) return st;
+  REQUIRE(q && k && v && o, "q, k, v and o must be non-NULL");
+  REQUIRE(ld_q_h >= static_cast<int64_t>(N) * VELOX_BLOCK * d,
+          "ld_q_h=%lld is smaller than N*128*d=%lld", static_cast<long long>(ld_q_h),
+          static_cast<long long>(N) * VELOX_BLOCK * d);
+  REQUIRE(ld_kv_h >= static_cast<int64_t>(M + N) * VELOX_BLOCK * d,
+          "ld_kv_h=%lld is smaller than (M+N)*128*d=%lld", static_cast<long long>(ld_kv_h),
+          static_cast<long long>(M + N) * VELOX_BLOCK * d);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, "scale must be finite and > 0");
+  const size_t align = dt == VELOX_BF16 ? 16 : 16;
+  REQUIRE(reinterpret_cast<uintptr_t>(q) % align == 0 && reinterpret_cast<uintptr_t>(k) % align == 0 &&
+              reinterpret_cast<uintptr_t>(v) % align == 0 && reinterpret_cast<uintptr_t>(o) % align == 0,
+          "q, k, v and o must be 16-byte aligned");
+  REQUIRE(ld_q_h % 8 == 0 && ld_kv_h % 8 == 0, "head strides must be multiples of 8 elements");
+  return VELOX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* velox_last_error(void) { return g_last_error.c_str(); }
+
+int velox_version(void) { return 100; }
+
+velox_status_t velox_block_mean(const void* x, velox_dtype_t dt, int64_t ld_x_h, int H, int nblk,
+                                int d, float* xbar, int64_t ld_bar_h, void* stream) {
+  REQUIRE(dtype_ok(dt), "dtype must be VELOX_F32 or VELOX_BF16");
+  REQUIRE(dim_ok(d), "d must be 64 or 128 (got %d)", d);
+  REQUIRE(H >= 1 && nblk >= 0, "need H >= 1 and nblk >= 0 (got H=%d nblk=%d)", H, nblk);
+  if (nblk == 0) return VELOX_OK;
+  REQUIRE(x && xbar, "x and xbar must be non-NULL");
+  REQUIRE(ld_x_h >= static_cast<int64_t>(nblk) * VELOX_BLOCK * d, "ld_x_h too small");
+  REQUIRE(ld_bar_h >= static_cast<int64_t>(nblk) * d, "ld_bar_h too small");
+  return launched(velox::launch_block_mean(x, dt == VELOX_BF16, ld_x_h, H, nblk, d, xbar, ld_bar_h,
+                                           static_cast<hipStream_t>(stream)),
+                  "velox_block_mean");
+}
+
+velox_status_t velox_route_scores(const void* q, velox_dtype_t dt, int64_t ld_q_h,
+                                  const float* kbar, int64_t ld_kbar_h, int H, int N, int M, int d,
+                                  float scale, float* p, void* stream) {
+  velox_status_t st = check_common(dt, H, N, M, d);
+  if (st != VELOX_OK) return st;
+  if (M == 0) return VELOX_OK;
+  REQUIRE(q && kbar && p, "q, kbar and p must be non-NULL");
+  REQUIRE(ld_q_h >= static_cast<int64_t>(N) * VELOX_BLOCK * d, "ld_q_h too small");
+  REQUIRE(ld_kbar_h >= static_cast<int64_t>(M) * d, "ld_kbar_h too small");
+  REQUIRE(std::isfinite(scale), "scale must be finite");
+  if (velox::route_scores_lds_bytes(1, M, d) > velox::kMaxLdsBytes)
+    return fail(VELOX_ERR_UNSUPPORTED, "M=%d too large for route_scores", M);
+  return launched(velox::launch_route_scores(q, dt == VELOX_BF16, ld_q_h, kbar, ld_kbar_h, H, N, M, d,
+                                             scale, p, static_cast<hipStream_t>(stream)),
+                  "velox_route_scores");
+}
+
+velox_status_t velox_route_select(const float* p, const float* g, const float* rho,
+                                  const int32_t* coord, int H, int N, int M,
+                                  const velox_route_params_t* prm, int L, int32_t* route_ids,
+                                  int32_t* route_len, void* stream) {
+  REQUIRE(prm, "prm must be non-NULL");
+  REQUIRE(H >= 1 && N >= 1 && M >= 0, "need H >= 1, N >= 1, M >= 0 (got H=%d N=%d M=%d)", H, N, M);
+  if (M > VELOX_MAX_HISTORY)
+    return fail(VELOX_ERR_UNSUPPORTED, "M=%d exceeds VELOX_MAX_HISTORY=%d", M, VELOX_MAX_HISTORY);
+  REQUIRE(route_ids && route_len, "route_ids and route_len must be non-NULL");
+  REQUIRE(M == 0 || (p && g && rho), "p, g and rho must be non-NULL when M > 0");
+  REQUIRE(!prm->neigh26 || coord, "coord must be non-NULL when neigh26 is set");
+  REQUIRE(prm->n_ref >= 0 && (prm->n_ref == 0 || prm->ref_ids), "ref_ids must hold n_ref ids");
+  REQUIRE(prm->K_cov >= 0 && prm->K_unc >= 0, "K_cov and K_unc must be >= 0");
+  REQUIRE(prm->n_prev >= 0 && prm->n_prev <= M, "n_prev must lie in [0, M] (got %d, M=%d)",
+          prm->n_prev, M);
+  REQUIRE(std::isfinite(prm->tau) && std::isfinite(prm->eta_cov), "tau and eta_cov must be finite");
+  REQUIRE(std::isfinite(prm->g_ref) && prm->g_ref > 0.f, "g_ref must be finite and > 0");
+  REQUIRE(prm->lambda >= 0.f && prm->lambda <= 14.f, "lambda must lie in [0, 14]");
+  REQUIRE(prm->theta_cov > 0.f && prm->theta_unc > 0.f, "theta_cov and theta_unc must be > 0");
+  REQUIRE(prm->neigh26 == 0 || prm->neigh26 == 1, "neigh26 must be 0 or 1");
+  const long long kmax = prm->K_cov > prm->K_unc ? prm->K_cov : prm->K_unc;
+  const long long base = kmax > prm->n_prev ? kmax : prm->n_prev;
+  long long need = base + 26LL * prm->neigh26 + prm->n_ref;
+  if (need > M) need = M;
+  if (need < 1) need = 1;
+  REQUIRE(L >= need, "L=%d is smaller than the route bound %lld", L, need);
+  velox::RouteConfig cfg{prm->tau,     prm->g_ref, prm->lambda, prm->eta_cov,
+                         prm->theta_cov, prm->theta_unc, prm->K_cov, prm->K_unc,
+                         prm->n_prev,  prm->neigh26, prm->ref_ids, prm->n_ref};
+  return launched(velox::launch_route_select(p, g, rho, coord, H, N, M, cfg, L, route_ids, route_len,
+                                             static_cast<hipStream_t>(stream)),
+                  "velox_route_select");
+}
+
+velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                                 int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                                 float scale, const int32_t* route_ids, const int32_t* route_len,
+                                 int L, int include_current, void* o, float* lse, void* stream) {
+  velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
+  if (st != VELOX_OK) return st;
+  REQUIRE(route_ids && route_len, "route_ids and route_len must be non-NULL");
+  REQUIRE(L >= 1, "L must be >= 1");
+  REQUIRE(include_current == 0 || include_current == 1, "include_current must be 0 or 1");
+  velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
+                      route_ids, route_len, L, include_current, o, lse};
+  return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), "velox_sparse_attn");
+}
+
+velox_status_t velox_dense_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                                int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                                float scale, void* o, float* lse, void* stream) {
+  velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
+  if (st != VELOX_OK) return st;
+  velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
+                      nullptr, nullptr, 0, 1, o, lse};
+  return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), "velox_dense_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace velox {
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+struct RouteConfig {
+  float tau, g_ref, lambda, eta_cov, theta_cov, theta_unc;
+  int K_cov, K_unc, n_prev, neigh26;
+  const int32_t* ref_ids;
+  int n_ref;
+};
+
+struct AttnConfig {
+  const void* q;
+  const void* k;
+  const void* v;
+  bool bf16;
+  int64_t ld_q_h, ld_kv_h;
+  int H, N, M, d;
+  float scale;
+  const int32_t* route_ids;  // nullptr: dense (every history tile)
+  const int32_t* route_len;
+  int L;
+  int include_current;
+  void* o;
+  float* lse;
+};
+
+hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, int nblk, int d,
+                             float* xbar, int64_t ld_bar_h, hipStream_t stream);
+size_t route_scores_lds_bytes(int qb, int M, int d);
+hipError_t launch_route_scores(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
+                               int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
+                               float* p, hipStream_t stream);
+size_t route_select_lds_bytes(int M);
+hipError_t launch_route_select(const float* p, const float* g, const float* rho,
+                               const int32_t* coord, int H, int N, int M, const RouteConfig& cfg,
+                               int L, int32_t* route_ids, int32_t* route_len, hipStream_t stream);
+hipError_t launch_attention(const AttnConfig& cfg, hipStream_t stream);
+
+}  // namespace velox

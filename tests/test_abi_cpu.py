@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects invalid arguments on the host before any launch. No GPU needed: every
+call below fails validation, so no device memory is ever touched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from geometry_routed_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "velox.h")
+
+BAD = 0x1000  # a non-NULL pointer value that validation must reject before use
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(velox_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert set(_declared()) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.velox_version() >= 100
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_block_mean_validation(lib):
+    f = lib.velox_block_mean
+    assert f(BAD, 0, 1 << 20, 1, 1, 96, BAD, 96, None) == _lib.VELOX_ERR_INVALID
+    assert b"d must be 64 or 128" in lib.velox_last_error()
+    assert f(BAD, 7, 1 << 20, 1, 1, 64, BAD, 64, None) == _lib.VELOX_ERR_INVALID
+    assert f(None, 0, 1 << 20, 1, 1, 64, BAD, 64, None) == _lib.VELOX_ERR_INVALID
+    assert f(BAD, 0, 10, 1, 1, 64, BAD, 64, None) == _lib.VELOX_ERR_INVALID    # ld too small
+    assert f(None, 0, 0, 1, 0, 64, None, 0, None) == _lib.VELOX_OK             # nblk = 0: no-op
+
+
+def test_route_scores_validation(lib):
+    f = lib.velox_route_scores
+    ok_ld = 4 * 128 * 64
+    assert f(BAD, 1, ok_ld, BAD, 64 * 16, 0, 4, 16, 64, ctypes.c_float(0.125), BAD, None) == _lib.VELOX_ERR_INVALID
+    assert f(BAD, 1, ok_ld, BAD, 64 * 16, 2, 4, -1, 64, ctypes.c_float(0.125), BAD, None) == _lib.VELOX_ERR_INVALID
+    assert f(BAD, 1, ok_ld, BAD, 64 * 16, 2, 4, 20000, 64, ctypes.c_float(0.125), BAD, None) == _lib.VELOX_ERR_UNSUPPORTED
+    assert f(BAD, 1, ok_ld, BAD, 10, 2, 4, 16, 64, ctypes.c_float(0.125), BAD, None) == _lib.VELOX_ERR_INVALID
+    assert f(BAD, 1, ok_ld, BAD, 64 * 16, 2, 4, 16, 64, ctypes.c_float(float("nan")), BAD, None) == _lib.VELOX_ERR_INVALID
+    # M = 0 writes nothing and launches nothing
+    assert f(BAD, 1, ok_ld, BAD, 0, 2, 4, 0, 64, ctypes.c_float(0.125), BAD, None) == _lib.VELOX_OK
+
+
+def _params(**kw):
+    base = dict(tau=0.1, g_ref=0.2, lambda_=2.0, eta_cov=0.9, theta_cov=1.0, theta_unc=0.9,
+                K_cov=80, K_unc=150, n_prev=0, neigh26=0, ref_ids=None, n_ref=0)
+    base.update(kw)
+    return _lib.RouteParamsC(**base)
+
+
+def test_route_select_validation(lib):
+    f = lib.velox_route_select
+
+    def call(prm, L=150, M=200, coord=BAD):
+        return f(BAD, BAD, BAD, coord, 2, 4, M, ctypes.byref(prm), L, BAD, BAD, None)
+
+    assert f(BAD, BAD, BAD, BAD, 2, 4, 200, None, 150, BAD, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert call(_params(), L=149) == _lib.VELOX_ERR_INVALID                 # L below the bound
+    assert b"route bound" in lib.velox_last_error()
+    assert call(_params(neigh26=1), L=150) == _lib.VELOX_ERR_INVALID       # needs 176
+    assert call(_params(neigh26=1), L=176, coord=None) == _lib.VELOX_ERR_INVALID
+    assert call(_params(g_ref=0.0)) == _lib.VELOX_ERR_INVALID
+    assert call(_params(lambda_=15.0)) == _lib.VELOX_ERR_INVALID
+    assert call(_params(theta_unc=0.0)) == _lib.VELOX_ERR_INVALID
+    assert call(_params(n_prev=201)) == _lib.VELOX_ERR_INVALID
+    assert call(_params(K_cov=-1)) == _lib.VELOX_ERR_INVALID
+    assert call(_params(n_ref=2)) == _lib.VELOX_ERR_INVALID                # NULL ref_ids
+    assert call(_params(), M=20000) == _lib.VELOX_ERR_UNSUPPORTED
+
+
+def test_attention_validation(lib):
+    sp, de = lib.velox_sparse_attn, lib.velox_dense_attn
+    H, N, M, d = 2, 4, 16, 64
+    ldq, ldkv = N * 128 * d, (M + N) * 128 * d
+    s = ctypes.c_float(0.125)
+    A = 0x10000  # aligned fake pointer
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, 80, s, A, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv - 1, H, N, M, d, s, A, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, None, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 0, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 2, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A + 2, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert de(A, A, A, 1, ldq, ldkv, H, N, M, d, ctypes.c_float(-1.0), A, None, None) == _lib.VELOX_ERR_INVALID
+    assert de(A, A, A, 1, ldq, ldkv, 0, N, M, d, s, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert de(None, A, A, 1, ldq, ldkv, H, N, M, d, s, A, None, None) == _lib.VELOX_ERR_INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()
