@@ -38,7 +38,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24,
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a "
+                         "known-size reference for HBM byte counters)")
+    ap.add_argument("--cpu-rows", type=int, default=480,
                     help="query-block rows of the oracle's attention sample")
     return ap.parse_args()
 
@@ -135,6 +138,14 @@ def main():
     lens = torch.empty(wl.H, wl.N, dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src_buf = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        del src_buf, dst_buf
 
     def step():
         velox.route_scores(q, kbar, wl.M, out=p)

@@ -38,6 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 struct AttnArgs {
@@ -80,23 +81,23 @@ struct TileShape {
 };
 
 template <int D>
-__device__ __forceinline__ void tile_gload(uint4 (&r)[TileShape<D>::kPasses],
+__device__ __forceinline__ void tile_gload(u32x4_t (&r)[TileShape<D>::kPasses],
                                            const bf16_t* __restrict__ src, int t) {
   using S = TileShape<D>;
   const int row = t / S::kChunksPerRow, col = (t % S::kChunksPerRow) * 8;
 #pragma unroll
   for (int ps = 0; ps < S::kPasses; ++ps)
-    r[ps] = *reinterpret_cast<const uint4*>(src + (ps * S::kRowsPerPass + row) * D + col);
+    r[ps] = *reinterpret_cast<const u32x4_t*>(src + (ps * S::kRowsPerPass + row) * D + col);
 }
 
 template <int D>
-__device__ __forceinline__ void tile_lstore(bf16_t* lds, const uint4 (&r)[TileShape<D>::kPasses],
+__device__ __forceinline__ void tile_lstore(bf16_t* lds, const u32x4_t (&r)[TileShape<D>::kPasses],
                                             int t) {
   using S = TileShape<D>;
   const int row = t / S::kChunksPerRow, col = (t % S::kChunksPerRow) * 8;
 #pragma unroll
   for (int ps = 0; ps < S::kPasses; ++ps)
-    *reinterpret_cast<uint4*>(lds + (ps * S::kRowsPerPass + row) * S::kLdsStride + col) = r[ps];
+    *reinterpret_cast<u32x4_t*>(lds + (ps * S::kRowsPerPass + row) * S::kLdsStride + col) = r[ps];
 }
 
 template <int D, bool kRouted>
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int ds = 0; ds < kDs; ++ds)
     qf[ds] = __builtin_bit_cast(
-        bf16x8_t, *reinterpret_cast<const uint4*>(qh + static_cast<int64_t>(qrow) * D + ds * 16 + hh * 8));
+        bf16x8_t, *reinterpret_cast<const u32x4_t*>(qh + static_cast<int64_t>(qrow) * D + ds * 16 + hh * 8));
 
   f32x16_t o_acc[kDb];
 #pragma unroll
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;        // this lane's share of the running sum
   const float sc = a.scale * 1.4426950408889634f;
 
-  uint4 kreg[S::kPasses], vreg[S::kPasses];
   {
+    u32x4_t kreg[S::kPasses], vreg[S::kPasses];
     const int t0 = tile_at<kRouted>(route, rlen, M, 0);
     tile_gload<D>(kreg, kh + static_cast<int64_t>(t0) * kBlock * D, t);
     tile_gload<D>(vreg, vh + static_cast<int64_t>(t0) * kBlock * D, t);
@@ -159,21 +160,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     tile_lstore<D>(v_lds, vreg, t);
   }
   __syncthreads();
-  if (T > 1) {
-    const int t1 = tile_at<kRouted>(route, rlen, M, 1);
-    tile_gload<D>(kreg, kh + static_cast<int64_t>(t1) * kBlock * D, t);
-  }
 
   // LDS addresses of this lane's operand fragments
   const bf16_t* k_frag = k_lds + l32 * S::kLdsStride + hh * 8;
   const int grp = lane / 16, gi = lane % 16;
   const bf16_t* v_frag = v_lds + (hh * 4 + gi / 4) * S::kLdsStride + 16 * (grp % 2) + 4 * (gi % 4);
 
+  // Per tile j: the K tile of j+1 is fetched into registers while S(j) is
+  // computed and written to LDS once every wave is done with K(j); the V tile
+  // of j+1 is fetched during softmax / PV(j) and written after it. The staging
+  // registers never live across iterations.
   for (int j = 0; j < T; ++j) {
-    if (j + 1 < T) {
-      const int tn = tile_at<kRouted>(route, rlen, M, j + 1);
-      tile_gload<D>(vreg, vh + static_cast<int64_t>(tn) * kBlock * D, t);
-    }
+    const bool more = j + 1 < T;
+    // On the last step the loads re-read tile j (always in bounds) and are
+    // discarded; loading unconditionally keeps the staging array in registers.
+    const int tn = tile_at<kRouted>(route, rlen, M, more ? j + 1 : j);
+    u32x4_t kreg[S::kPasses];
+    tile_gload<D>(kreg, kh + static_cast<int64_t>(tn) * kBlock * D, t);
 
     // ---- S^T = K Q^T : 4 key blocks of 32
     f32x16_t s_acc[4];
@@ -183,18 +186,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int ds = 0; ds < kDs; ++ds) {
         const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(k_frag + kb * 32 * S::kLdsStride + ds * 16));
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(k_frag + kb * 32 * S::kLdsStride + ds * 16));
         s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s_acc[kb], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with k_lds(j)
-    if (j + 1 < T) {
-      tile_lstore<D>(k_lds, kreg, t);
-      if (j + 2 < T) {
-        const int tn = tile_at<kRouted>(route, rlen, M, j + 2);
-        tile_gload<D>(kreg, kh + static_cast<int64_t>(tn) * kBlock * D, t);
-      }
-    }
+    __syncthreads();  // every wave is done with k_lds(j); v_lds(j) is visible
+    u32x4_t vreg[S::kPasses];
+    if (more) tile_lstore<D>(k_lds, kreg, t);
+    tile_gload<D>(vreg, vh + static_cast<int64_t>(tn) * kBlock * D, t);
 
     // ---- online softmax (this lane: one query, 64 of the tile's 128 keys)
     float mx = s_acc[0][0];
@@ -238,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     __syncthreads();  // every wave is done with v_lds(j); k_lds(j+1) is visible
-    if (j + 1 < T) tile_lstore<D>(v_lds, vreg, t);
+    if (more) tile_lstore<D>(v_lds, vreg, t);
   }
 
   // ---- normalise and store

@@ -93,78 +93,131 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x
 
 // ---------------------------------------------------------------- importance
 //
-// One workgroup per (group of QB query blocks, head). The query means are
-// reduced into LDS, key means stream through LDS 64 blocks at a time, the
-// logits of the QB rows stay in LDS, and each row is soft-maxed in place.
+// One workgroup (512 threads) per (group of QB query blocks, head).
+//  1. query block means: 16-byte loads, all QB blocks' loads in flight, then a
+//     reduction over row groups in LDS.
+//  2. logits: each thread owns history blocks r = t, t + 512, ...; it streams
+//     kbar[h][r] with 16-byte loads and dots it with the QB query means, which
+//     are broadcast from LDS. Logits of the QB rows stay in LDS.
+//  3. softmax over the history blocks of each row, written coalesced.
 
-constexpr int kScoreTile = 64;
+constexpr int kScoreThreads = 512;
 
-template <typename T, int QB>
-__global__ __launch_bounds__(256) void route_scores_kernel(const T* __restrict__ q, int64_t ld_q_h,
-                                                           const float* __restrict__ kbar,
-                                                           int64_t ld_kbar_h, int N, int M, int d,
-                                                           float scale, float* __restrict__ p) {
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(w[j] << 16);
+    x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <typename T, int D, int QB>
+__global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
+    const T* __restrict__ q, int64_t ld_q_h, const float* __restrict__ kbar, int64_t ld_kbar_h,
+    int N, int M, float scale, float* __restrict__ p) {
+  constexpr int kCpr = D / 8;                      // 8-element chunks per token row
+  constexpr int kGroups = kScoreThreads / kCpr;    // token-row groups
+  constexpr int kPasses = kBlock / kGroups;
   extern __shared__ float smem[];
-  float* qbar = smem;                              // [QB][d]
-  float* ktile = qbar + QB * d;                    // [64][d + 1]
-  float* logit = ktile + kScoreTile * (d + 1);     // [QB][M]
-  float* red = logit + QB * M;                     // [256]
+  float* qbar = smem;                              // [QB][D]
+  float* red = qbar + QB * D;                      // [kGroups][D]
+  float* logit = red + kGroups * D;                // [QB][M]
   const int h = blockIdx.y, i0 = blockIdx.x * QB, t = threadIdx.x;
   const int nq = min(QB, N - i0);
 
-  // 1. query block means
-  const int parts = 256 / d, c = t % d, s = t / d;
-  for (int qb = 0; qb < nq; ++qb) {
-    const T* src = q + h * ld_q_h + static_cast<int64_t>(i0 + qb) * kBlock * d;
-    float acc = 0.f;
-    for (int a = s; a < kBlock; a += parts) acc += load_f32(src + a * d + c);
-    red[t] = acc;
-    __syncthreads();
-    if (t < d) {
-      float tot = 0.f;
-      for (int j = 0; j < parts; ++j) tot += red[j * d + t];
-      qbar[qb * d + t] = tot * (1.0f / kBlock);
-    }
-    __syncthreads();
-  }
-
-  // 2. logits = scale * qbar . kbar
-  const float* kb = kbar + h * ld_kbar_h;
-  const int rr = t % kScoreTile, grp = t / kScoreTile;  // grp is the wave index
-  for (int r0 = 0; r0 < M; r0 += kScoreTile) {
-    const int nr = min(kScoreTile, M - r0);
-    for (int e = t; e < nr * d; e += 256) {
-      const int er = e / d, ec = e % d;
-      ktile[er * (d + 1) + ec] = kb[static_cast<int64_t>(r0 + er) * d + ec];
-    }
-    __syncthreads();
-    if (rr < nr) {
-      for (int qb = grp; qb < nq; qb += 4) {
-        float acc = 0.f;
-        const float* qv = qbar + qb * d;
-        const float* kv = ktile + rr * (d + 1);
-        for (int cc = 0; cc < d; ++cc) acc = fmaf(qv[cc], kv[cc], acc);
-        logit[qb * M + r0 + rr] = acc * scale;
+  // 1. query block means, two blocks' loads in flight at a time
+  {
+    const int c8 = t % kCpr, grp = t / kCpr;
+    for (int qb0 = 0; qb0 < nq; qb0 += 2) {
+      const int nb = min(2, nq - qb0);
+      float acc[2][8];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+        if (b < nb) {
+          const T* src = q + h * ld_q_h + static_cast<int64_t>(i0 + qb0 + b) * kBlock * D + c8 * 8;
+#pragma unroll
+          for (int ps = 0; ps < kPasses; ++ps) {
+            float x[8];
+            load8<T>(src + (ps * kGroups + grp) * D, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[b][e] += x[e];
+          }
+        }
+      }
+      for (int b = 0; b < nb; ++b) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[grp * D + c8 * 8 + e] = b == 0 ? acc[0][e] : acc[1][e];
+        __syncthreads();
+        if (t < D) {
+          float s = 0.f;
+          for (int g2 = 0; g2 < kGroups; ++g2) s += red[g2 * D + t];
+          qbar[(qb0 + b) * D + t] = s * (1.0f / kBlock);
+        }
+        __syncthreads();
       }
     }
-    __syncthreads();
   }
+
+  // 2. logits
+  const float* kb = kbar + h * ld_kbar_h;
+  for (int r = t; r < M; r += kScoreThreads) {
+    const float4* krow = reinterpret_cast<const float4*>(kb + static_cast<int64_t>(r) * D);
+    float dot[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) dot[qb] = 0.f;
+    // not unrolled: keeps the loop-invariant query means in LDS, not registers
+#pragma unroll 1
+    for (int c0 = 0; c0 < D / 4; c0 += 8) {
+      float4 kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = krow[c0 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float4 qv = reinterpret_cast<const float4*>(qbar + qb * D)[c0 + u];
+          dot[qb] = fmaf(qv.x, kv[u].x, dot[qb]);
+          dot[qb] = fmaf(qv.y, kv[u].y, dot[qb]);
+          dot[qb] = fmaf(qv.z, kv[u].z, dot[qb]);
+          dot[qb] = fmaf(qv.w, kv[u].w, dot[qb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (qb < nq) logit[qb * M + r] = dot[qb] * scale;
+  }
+  __syncthreads();
 
   // 3. softmax over the history blocks of each row
   for (int qb = 0; qb < nq; ++qb) {
     float* lr = logit + qb * M;
     float mx = -INFINITY;
-    for (int r = t; r < M; r += 256) mx = fmaxf(mx, lr[r]);
+    for (int r = t; r < M; r += kScoreThreads) mx = fmaxf(mx, lr[r]);
     mx = block_max(mx, red);
     float sum = 0.f;
-    for (int r = t; r < M; r += 256) {
+    for (int r = t; r < M; r += kScoreThreads) {
       const float e = expf(lr[r] - mx);
       lr[r] = e;
       sum += e;
     }
     sum = block_sum(sum, red);
     float* out = p + (static_cast<int64_t>(h) * N + i0 + qb) * M;
-    for (int r = t; r < M; r += 256) out[r] = lr[r] / sum;
+    for (int r = t; r < M; r += kScoreThreads) out[r] = lr[r] / sum;
   }
 }
 
@@ -393,35 +446,46 @@ hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, in
 }
 
 size_t route_scores_lds_bytes(int qb, int M, int d) {
-  return sizeof(float) * (static_cast<size_t>(qb) * d + kScoreTile * (d + 1) +
-                          static_cast<size_t>(qb) * M + 256);
+  const int groups = kScoreThreads / (d / 8);
+  return sizeof(float) * (static_cast<size_t>(qb) * d + static_cast<size_t>(groups) * d +
+                          static_cast<size_t>(qb) * M);
 }
 
-template <typename T, int QB>
+template <typename T, int D, int QB>
 static hipError_t scores_launch(const void* q, int64_t ld_q_h, const float* kbar,
-                                int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
-                                float* p, hipStream_t stream) {
-  const size_t lds = route_scores_lds_bytes(QB, M, d);
-  auto kern = route_scores_kernel<T, QB>;
+                                int64_t ld_kbar_h, int H, int N, int M, float scale, float* p,
+                                hipStream_t stream) {
+  const size_t lds = route_scores_lds_bytes(QB, M, D);
+  auto kern = route_scores_kernel<T, D, QB>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
   dim3 grid((N + QB - 1) / QB, H);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, static_cast<const T*>(q), ld_q_h, kbar,
-                     ld_kbar_h, N, M, d, scale, p);
+  hipLaunchKernelGGL(kern, grid, dim3(kScoreThreads), lds, stream, static_cast<const T*>(q),
+                     ld_q_h, kbar, ld_kbar_h, N, M, scale, p);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t scores_dispatch(const void* q, int64_t ld_q_h, const float* kbar,
+                                  int64_t ld_kbar_h, int H, int N, int M, float scale, float* p,
+                                  hipStream_t stream) {
+  if (route_scores_lds_bytes(6, M, D) <= kMaxLdsBytes)
+    return scores_launch<T, D, 6>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+  if (route_scores_lds_bytes(3, M, D) <= kMaxLdsBytes)
+    return scores_launch<T, D, 3>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+  return scores_launch<T, D, 1>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
 }
 
 hipError_t launch_route_scores(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
                                int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
                                float* p, hipStream_t stream) {
-  const bool wide = route_scores_lds_bytes(4, M, d) <= kMaxLdsBytes;
   if (bf16)
-    return wide ? scores_launch<bf16_t, 4>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, d, scale, p, stream)
-                : scores_launch<bf16_t, 1>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, d, scale, p, stream);
-  return wide ? scores_launch<float, 4>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, d, scale, p, stream)
-              : scores_launch<float, 1>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, d, scale, p, stream);
+    return d == 128 ? scores_dispatch<bf16_t, 128>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream)
+                    : scores_dispatch<bf16_t, 64>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+  return d == 128 ? scores_dispatch<float, 128>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream)
+                  : scores_dispatch<float, 64>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
 }
 
 size_t route_select_lds_bytes(int M) {
