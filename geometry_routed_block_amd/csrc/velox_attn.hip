@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "velox_device.hpp"
 #include "velox_launch.hpp"
 
@@ -40,6 +42,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 struct AttnArgs {
   const void* q;
@@ -56,57 +59,168 @@ struct AttnArgs {
   float* lse;
 };
 
-// Tile id of step j of a row: routed history tiles first, then the current
-// chunk. Out-of-range route ids are clamped into [0, M) (never read out of bounds).
+// Tile id of step j of a row. The current chunk's tiles come first (ncur of
+// them: N, or 0 without the current chunk): every query block of a head
+// visits them, so taking them together at the start lets the blocks of one
+// head share them in L2. The routed (or, dense, all) history tiles follow in
+// ascending id order. Out-of-range route ids are clamped into [0, M) (never
+// read out of bounds).
 template <bool kRouted>
-__device__ __forceinline__ int tile_at(const int32_t* route, int rlen, int M, int j) {
-  if (kRouted) {
-    if (j < rlen) {
-      const int id = route[j];
-      return min(max(id, 0), M - 1);
-    }
-    return M + (j - rlen);
-  }
+__device__ __forceinline__ int tile_at(const int32_t* route, int ncur, int M, int j) {
+  if (j < ncur) return M + j;
+  j -= ncur;
+  if (kRouted) return min(max(route[j], 0), M - 1);
   return j;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
 
+// LDS layout of one 128-token K or V tile (bf16). kSwz (d = 128 only): rows of
+// d elements whose 16-byte chunks are XOR-permuted, chunk c of row r stored at
+// c ^ (r mod 16) for K and c ^ (4 r mod 16) for V. Those are the permutations
+// under which the K fragment reads (16 B per lane, 32 rows x one chunk) and
+// the V transpose reads (8 B per lane, 4 rows x two chunks per 16 lanes) hit
+// distinct LDS banks. Otherwise rows are padded (K: d + 8, V: d + 32 elements),
+// which has the same property at the cost of LDS space.
+template <int D, bool kSwz>
+struct Layout {
+  static_assert(!kSwz || D == 128, "the swizzled layout is defined for d = 128");
+  static constexpr int kCpr = D / 8;                         // 16-byte chunks per row
+  static constexpr int kKStride = kSwz ? D : D + 8;
+  static constexpr int kVStride = kSwz ? D : D + 32;
+  static constexpr int kKElems = kBlock * kKStride;
+  static constexpr int kVElems = kBlock * kVStride;
+  __device__ static __forceinline__ int k_off(int row, int c) {
+    return row * kKStride + (kSwz ? ((c ^ (row & 15)) << 3) : (c << 3));
+  }
+  __device__ static __forceinline__ int v_off(int row, int c) {
+    return row * kVStride + (kSwz ? ((c ^ ((row << 2) & 15)) << 3) : (c << 3));
+  }
+};
+
+// Register-staged tile copy: 256 threads, 16 bytes each per pass.
 template <int D>
-struct TileShape {
-  static constexpr int kChunksPerRow = D / 8;             // 16-byte chunks per token row
-  static constexpr int kRowsPerPass = 256 / kChunksPerRow;
+struct Stage {
+  static constexpr int kCpr = D / 8;
+  static constexpr int kRowsPerPass = 256 / kCpr;
   static constexpr int kPasses = kBlock / kRowsPerPass;
-  static constexpr int kLdsStride = D + 8;                 // bf16 elements per LDS row
 };
 
 template <int D>
-__device__ __forceinline__ void tile_gload(u32x4_t (&r)[TileShape<D>::kPasses],
+__device__ __forceinline__ void tile_gload(u32x4_t (&r)[Stage<D>::kPasses],
                                            const bf16_t* __restrict__ src, int t) {
-  using S = TileShape<D>;
-  const int row = t / S::kChunksPerRow, col = (t % S::kChunksPerRow) * 8;
+  using S = Stage<D>;
+  const int row = t / S::kCpr, col = (t % S::kCpr) * 8;
 #pragma unroll
   for (int ps = 0; ps < S::kPasses; ++ps)
     r[ps] = *reinterpret_cast<const u32x4_t*>(src + (ps * S::kRowsPerPass + row) * D + col);
 }
 
-template <int D>
-__device__ __forceinline__ void tile_lstore(bf16_t* lds, const u32x4_t (&r)[TileShape<D>::kPasses],
+template <int D, bool kSwz, bool kIsV>
+__device__ __forceinline__ void tile_lstore(bf16_t* lds, const u32x4_t (&r)[Stage<D>::kPasses],
                                             int t) {
-  using S = TileShape<D>;
-  const int row = t / S::kChunksPerRow, col = (t % S::kChunksPerRow) * 8;
+  using S = Stage<D>;
+  using Lay = Layout<D, kSwz>;
+  const int row0 = t / S::kCpr, c = t % S::kCpr;
 #pragma unroll
-  for (int ps = 0; ps < S::kPasses; ++ps)
-    *reinterpret_cast<u32x4_t*>(lds + (ps * S::kRowsPerPass + row) * S::kLdsStride + col) = r[ps];
+  for (int ps = 0; ps < S::kPasses; ++ps) {
+    const int row = ps * S::kRowsPerPass + row0;
+    const int off = kIsV ? Lay::v_off(row, c) : Lay::k_off(row, c);
+    *reinterpret_cast<u32x4_t*>(lds + off) = r[ps];
+  }
 }
 
-template <int D, bool kRouted>
+// Direct global -> LDS tile copy (gfx950 global_load_lds_dwordx4): wave w
+// fills LDS bytes [w * 8 KiB, (w + 1) * 8 KiB) of the tile, 1 KiB (4 rows) per
+// instruction; lane l of instruction i lands at row (8 w + i) * 4 + l / 16,
+// physical chunk l % 16, so it fetches the logical chunk that the swizzle puts
+// there. d = 128, swizzled layout only.
+template <bool kIsV>
+__device__ __forceinline__ void tile_dload(bf16_t* lds, const bf16_t* __restrict__ src, int wv,
+                                           int lane) {
+  constexpr int D = 128;
+  const int wu = __builtin_amdgcn_readfirstlane(wv);
+  __attribute__((address_space(3))) char* dst =
+      (__attribute__((address_space(3))) char*)(lds) + wu * 8192;
+  const int p = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (wu * 8 + i) * 4 + (lane >> 4);
+    const int c = kIsV ? (p ^ ((row << 2) & 15)) : (p ^ (row & 15));
+    __builtin_amdgcn_global_load_lds(src + row * D + c * 8, dst + i * 1024, 16, 0, 0);
+  }
+}
+
+// Direct global -> LDS copy into the padded layout: the tile's LDS image
+// (128 rows of kStride elements) is filled 1 KiB per wave instruction, lane l
+// landing at byte 16 l of its instruction's KiB; lanes whose slot falls in a
+// row's padding are masked off.
+template <int D, int kStride>
+__device__ __forceinline__ void tile_dload_pad(bf16_t* lds, const bf16_t* __restrict__ src,
+                                               int wv, int lane) {
+  constexpr int kRowBytes = D * 2, kStrideBytes = kStride * 2;
+  constexpr int kInst = (kBlock * kStrideBytes + 1023) / 1024;
+  constexpr int kPerWave = (kInst + 3) / 4;
+  const int wu = __builtin_amdgcn_readfirstlane(wv);
+  __attribute__((address_space(3))) char* base = (__attribute__((address_space(3))) char*)(lds);
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int inst = wu * kPerWave + i;
+    if (inst < kInst) {
+      const int o = inst * 1024 + lane * 16;
+      const int row = o / kStrideBytes, rem = o - row * kStrideBytes;
+      if (rem < kRowBytes && row < kBlock)
+        __builtin_amdgcn_global_load_lds(src + row * D + rem / 2, base + inst * 1024, 16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence: the direct LDS loads are ordered
+// with explicit vmcnt waits, and a fence here would drain loads still meant to
+// be in flight.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct-LDS instructions each wave issues for one K (kK) or V (kV) tile.
+template <int D, bool kSwz>
+struct DmaCount {
+  static constexpr int kK = kSwz ? 8 : ((kBlock * Layout<D, false>::kKStride * 2 + 1023) / 1024 + 3) / 4;
+  static constexpr int kV = kSwz ? 8 : ((kBlock * Layout<D, false>::kVStride * 2 + 1023) / 1024 + 3) / 4;
+};
+
+constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int kMaxRouteLds = 4096;    // route ids staged in LDS by the DMA kernel
+
+template <int D, bool kSwz, bool kIsV>
+__device__ __forceinline__ void dload(bf16_t* lds, const bf16_t* __restrict__ src, int wv, int lane) {
+  if constexpr (kSwz)
+    tile_dload<kIsV>(lds, src, wv, lane);
+  else
+    tile_dload_pad<D, kIsV ? Layout<D, false>::kVStride : Layout<D, false>::kKStride>(lds, src, wv, lane);
+}
+
+template <int D, bool kRouted, bool kSwz, bool kDirect>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-  using S = TileShape<D>;
+  static_assert(!kDirect || D == 128, "direct LDS loads are written for d = 128");
+  using Lay = Layout<D, kSwz>;
+  using S = Stage<D>;
   constexpr int kDs = D / 16;   // 16-dim MFMA steps of QK^T
   constexpr int kDb = D / 32;   // 32-dim output blocks of PV
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[kBlock * S::kLdsStride];
-  __shared__ __attribute__((aligned(16))) bf16_t v_lds[kBlock * S::kLdsStride];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds[Lay::kKElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds[Lay::kVElems];
+  // With direct LDS loads the route is staged in LDS, so reading tile ids
+  // never puts a vector load in front of the DMA waits.
+  constexpr bool kRouteInLds = kRouted && kDirect;
+  __shared__ int route_lds[kRouteInLds ? kMaxRouteLds : 1];
 
   const int row_id = xcd_remap(blockIdx.x, a.G);
   const int h = row_id / a.N, i = row_id % a.N;
@@ -124,7 +238,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     rlen = min(max(a.route_len[row_id], 0), a.L);
     if (M == 0) rlen = 0;
   }
-  const int T = kRouted ? rlen + (a.include_current ? a.N : 0) : M + a.N;
+  const int ncur = (!kRouted || a.include_current) ? a.N : 0;
+  const int T = rlen + ncur;
 
   const int qrow = i * kBlock + wv * 32 + l32;  // this lane's query (token row)
   bf16_t* orow = static_cast<bf16_t*>(a.o) + (static_cast<int64_t>(h) * a.N * kBlock + qrow) * D;
@@ -147,36 +262,60 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   f32x16_t o_acc[kDb];
 #pragma unroll
   for (int db = 0; db < kDb; ++db) o_acc[db] = f32x16_t{};
-  float m_run = -INFINITY;  // running max of scaled logits (log2 units)
+  float m_ref = -INFINITY;  // reference max of the scaled logits (log2 units)
   float l_run = 0.f;        // this lane's share of the running sum
   const float sc = a.scale * 1.4426950408889634f;
 
+  // LDS element offsets of this lane's operand fragments.
+  //   K (A operand of S^T): row kb*32 + l32, chunk 2 ds + hh.
+  //   V (transpose read, A operand of O^T): rows ks*16 + hh*4 + gi/4 (+8),
+  //   chunk 4 db + 2 (grp & 1) + (gi & 3) / 2, half-chunk gi & 1.
+  const int grp = lane / 16, gi = lane % 16;
+  const int vrow = hh * 4 + gi / 4;
+  const int vsub = (gi & 1) * 4;
+
+  if constexpr (kRouteInLds) {
+    for (int e = t; e < rlen; e += 256) route_lds[e] = min(max(route[e], 0), M - 1);
+    __syncthreads();
+  }
+  auto tile_ptr = [&](const bf16_t* base, int j) {
+    int tile;
+    if constexpr (kRouteInLds)
+      tile = j < ncur ? M + j : route_lds[j - ncur];
+    else
+      tile = tile_at<kRouted>(route, ncur, M, j);
+    return base + static_cast<int64_t>(tile) * kBlock * D;
+  };
+
   {
-    u32x4_t kreg[S::kPasses], vreg[S::kPasses];
-    const int t0 = tile_at<kRouted>(route, rlen, M, 0);
-    tile_gload<D>(kreg, kh + static_cast<int64_t>(t0) * kBlock * D, t);
-    tile_gload<D>(vreg, vh + static_cast<int64_t>(t0) * kBlock * D, t);
-    tile_lstore<D>(k_lds, kreg, t);
-    tile_lstore<D>(v_lds, vreg, t);
+    if constexpr (kDirect) {
+      dload<D, kSwz, false>(k_lds, tile_ptr(kh, 0), wv, lane);
+      dload<D, kSwz, true>(v_lds, tile_ptr(vh, 0), wv, lane);
+      wait_vm_all();
+    } else {
+      u32x4_t kreg[S::kPasses], vreg[S::kPasses];
+      tile_gload<D>(kreg, tile_ptr(kh, 0), t);
+      tile_gload<D>(vreg, tile_ptr(vh, 0), t);
+      tile_lstore<D, kSwz, false>(k_lds, kreg, t);
+      tile_lstore<D, kSwz, true>(v_lds, vreg, t);
+    }
   }
   __syncthreads();
 
-  // LDS addresses of this lane's operand fragments
-  const bf16_t* k_frag = k_lds + l32 * S::kLdsStride + hh * 8;
-  const int grp = lane / 16, gi = lane % 16;
-  const bf16_t* v_frag = v_lds + (hh * 4 + gi / 4) * S::kLdsStride + 16 * (grp % 2) + 4 * (gi % 4);
-
-  // Per tile j: the K tile of j+1 is fetched into registers while S(j) is
-  // computed and written to LDS once every wave is done with K(j); the V tile
-  // of j+1 is fetched during softmax / PV(j) and written after it. The staging
-  // registers never live across iterations.
+  // Per tile j. Register-staged path: K(j+1) is fetched into registers during
+  // S(j) and stored once every wave is done with K(j); V(j+1) is fetched
+  // during softmax / PV(j) and stored after it. DMA path: K(j+1) is issued as
+  // soon as every wave is done with K(j) and must land before S(j+1); V(j+1)
+  // is issued once every wave is done with V(j) and must land before PV(j+1),
+  // so each load overlaps about half a tile of MFMA work plus a softmax.
   for (int j = 0; j < T; ++j) {
     const bool more = j + 1 < T;
-    // On the last step the loads re-read tile j (always in bounds) and are
-    // discarded; loading unconditionally keeps the staging array in registers.
-    const int tn = tile_at<kRouted>(route, rlen, M, more ? j + 1 : j);
+    // On the last step the staged loads re-read tile j (always in bounds) and
+    // are discarded; loading unconditionally keeps the staging in registers.
+    const bf16_t* kn = tile_ptr(kh, more ? j + 1 : j);
+    const bf16_t* vn = tile_ptr(vh, more ? j + 1 : j);
     u32x4_t kreg[S::kPasses];
-    tile_gload<D>(kreg, kh + static_cast<int64_t>(tn) * kBlock * D, t);
+    if constexpr (!kDirect) tile_gload<D>(kreg, kn, t);
 
     // ---- S^T = K Q^T : 4 key blocks of 32
     f32x16_t s_acc[4];
@@ -186,58 +325,90 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int ds = 0; ds < kDs; ++ds) {
         const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(k_frag + kb * 32 * S::kLdsStride + ds * 16));
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(k_lds + Lay::k_off(kb * 32 + l32, 2 * ds + hh)));
         s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s_acc[kb], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with k_lds(j); v_lds(j) is visible
     u32x4_t vreg[S::kPasses];
-    if (more) tile_lstore<D>(k_lds, kreg, t);
-    tile_gload<D>(vreg, vh + static_cast<int64_t>(tn) * kBlock * D, t);
+    if constexpr (kDirect) {
+      barrier_nofence();  // every wave is done with k_lds(j)
+      if (more) dload<D, kSwz, false>(k_lds, kn, wv, lane);
+    } else {
+      __syncthreads();    // every wave is done with k_lds(j); v_lds(j) is visible
+      if (more) tile_lstore<D, kSwz, false>(k_lds, kreg, t);
+      tile_gload<D>(vreg, vn, t);
+    }
 
-    // ---- online softmax (this lane: one query, 64 of the tile's 128 keys)
-    float mx = s_acc[0][0];
+    // ---- online softmax (this lane: one query, 64 of the tile's 128 keys).
+    // The reference max only moves when a score exceeds it by more than 2^8
+    // (then O and l are rescaled); otherwise every p stays below 2^8 and the
+    // final division is unaffected.
+    float mk[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      mk[kb] = s_acc[kb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_acc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+      for (int r = 1; r < 16; ++r) mk[kb] = fmaxf(mk[kb], s_acc[kb][r]);
+    }
+    float mx = fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+    if (__ballot(mx > m_ref + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDb; ++db) o_acc[db] *= alpha;
+    }
+    float ps[4];
     bf16x8_t pf[8];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f32x8_t lo, hi;
+      ps[kb] = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        lo[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][r], sc, -m_new));
-        hi[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][8 + r], sc, -m_new));
-        psum += lo[r] + hi[r];
+        lo[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][r], sc, -m_ref));
+        hi[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][8 + r], sc, -m_ref));
+        ps[kb] += lo[r] + hi[r];
       }
       pf[2 * kb] = __builtin_convertvector(lo, bf16x8_t);
       pf[2 * kb + 1] = __builtin_convertvector(hi, bf16x8_t);
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) o_acc[db] *= alpha;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+
+    if constexpr (kDirect) {
+      // this wave's part of V(j) has landed (K(j+1), issued later, may still fly)
+      if (more)
+        wait_vmcnt<DmaCount<D, kSwz>::kK>();
+      else
+        wait_vm_all();
+      barrier_nofence();  // v_lds(j) is visible
+    }
 
     // ---- O^T += V^T P^T : 8 key steps of 16
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int db = 0; db < kDb; ++db) {
-        const bf16_t* vp = v_frag + ks * 16 * S::kLdsStride + db * 32;
-        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp));
-        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 8 * S::kLdsStride));
+        const int vc = 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1);
+        const bf16_t* vp0 = v_lds + Lay::v_off(ks * 16 + vrow, vc) + vsub;
+        const bf16_t* vp1 = v_lds + Lay::v_off(ks * 16 + 8 + vrow, vc) + vsub;
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp0));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp1));
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o_acc[db], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with v_lds(j); k_lds(j+1) is visible
-    if (more) tile_lstore<D>(v_lds, vreg, t);
+    if constexpr (kDirect) {
+      wait_vm_all();      // this wave's part of K(j+1) has landed
+      barrier_nofence();  // every wave is done with v_lds(j); k_lds(j+1) is visible
+      if (more) dload<D, kSwz, true>(v_lds, vn, wv, lane);
+    } else {
+      __syncthreads();    // every wave is done with v_lds(j); k_lds(j+1) is visible
+      if (more) tile_lstore<D, kSwz, true>(v_lds, vreg, t);
+    }
   }
 
   // ---- normalise and store
@@ -255,8 +426,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   }
   if (a.lse && hh == 0)
-    a.lse[static_cast<int64_t>(h) * a.N * kBlock + qrow] = m_run * 0.6931471805599453f + logf(l_tot);
+    a.lse[static_cast<int64_t>(h) * a.N * kBlock + qrow] = m_ref * 0.6931471805599453f + logf(l_tot);
 }
+
 
 // ---------------------------------------------------------------- fp32
 //
@@ -283,7 +455,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     rlen = min(max(a.route_len[row_id], 0), a.L);
     if (M == 0) rlen = 0;
   }
-  const int T = kRouted ? rlen + (a.include_current ? a.N : 0) : M + a.N;
+  const int ncur = (!kRouted || a.include_current) ? a.N : 0;
+  const int T = rlen + ncur;
   const int qrow = i * kBlock + qr;
 
   float qv[kHalf], ov[kHalf];
@@ -294,7 +467,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
   float m_run = -INFINITY, l_run = 0.f;
   for (int j = 0; j < T; ++j) {
-    const int tile = tile_at<kRouted>(route, rlen, M, j);
+    const int tile = tile_at<kRouted>(route, ncur, M, j);
     const float4* ks = reinterpret_cast<const float4*>(kh + static_cast<int64_t>(tile) * kBlock * D);
     const float4* vs = reinterpret_cast<const float4*>(vh + static_cast<int64_t>(tile) * kBlock * D);
     __syncthreads();
@@ -331,8 +504,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int D, bool kRouted>
 static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream) {
-  if (bf16)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, kRouted>), dim3(args.G), dim3(256), 0, stream, args);
+  // d = 128: swizzled LDS tiles filled by direct DMA (routes of up to
+  // kMaxRouteLds tiles); otherwise padded tiles staged through registers.
+  const bool fast = D == 128 && (!kRouted || args.L <= kMaxRouteLds);
+  if (bf16 && fast)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, kRouted, D == 128, D == 128>), dim3(args.G), dim3(256),
+                       0, stream, args);
+  else if (bf16)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, kRouted, false, false>), dim3(args.G), dim3(256), 0,
+                       stream, args);
   else
     hipLaunchKernelGGL((attn_f32_kernel<D, kRouted>), dim3(args.G), dim3(256), 0, stream, args);
   return hipGetLastError();
