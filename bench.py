@@ -27,6 +27,26 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+KERNEL_SRC = os.path.join(ROOT, "geometry_routed_block_amd", "csrc", "velox_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sparse_chunk48_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per sparse-attention launch from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -244,12 +264,20 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
+            "traffic_note": None,
             "kernel": "attn_bf16_kernel<128, routed>",
             "hbm_unique_bytes": uniq_bytes,
             "hbm_frac_unique": round(uniq_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "cpu_baseline": None,
     }
+    tr = measured_traffic()
+    if tr is not None:
+        result["roofline"]["traffic"] = int(tr["fetch_bytes"] + tr["write_bytes"])
+        result["roofline"]["traffic_note"] = (
+            f"rocprofv3 FETCH_SIZE x{tr['fetch_scale']} + WRITE_SIZE x{tr['write_scale']} per launch "
+            f"(scales from a {tr['calib_mib']} MiB copy); fetch {tr['fetch_bytes'] / 1e9:.2f} GB, "
+            f"write {tr['write_bytes'] / 1e9:.3f} GB")
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, p, ids, lens, args.cpu_rows)

@@ -183,6 +183,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The same waits issued through the builtin (gfx9 s_waitcnt encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima), so that the
+// compiler's own wait insertion sees them and adds none of its own.
+__device__ __forceinline__ void tracked_wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+template <int N>
+__device__ __forceinline__ void tracked_wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier without a memory fence: the direct LDS loads are ordered
 // with explicit vmcnt waits, and a fence here would drain loads still meant to
 // be in flight.
@@ -430,6 +441,320 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 }
 
 
+// ---------------------------------------------------------------- bf16, d = 128, ping-pong
+//
+// Eight waves per workgroup in two teams of four. Each team owns one query
+// block (the two blocks of a workgroup belong to one head and are paired by
+// route length, so both teams run about the same number of tiles); each wave
+// owns 32 query rows of its team's block. Work advances in 64-key half-tiles,
+// and for every half-tile j a team runs
+//   an MFMA phase:  O += P(j-1) V(j-1)  and  S(j) = K(j) Q^T   (32 MFMAs/wave)
+//   a VALU phase:   softmax of S(j) -> P(j)                     (exp, max, sum)
+// The two teams are one phase apart, so on every SIMD one wave issues MFMAs
+// while the other runs its softmax; a fence-free workgroup barrier separates
+// phases. Each team has a two-slot ring for K and one for V (16 KiB slots,
+// 128 KiB in all); the DMA for K(j+2) and V(j+1) is issued at the start of VALU
+// phase j and has three phases to land before MFMA phase j+2 / j+1 needs it.
+
+namespace pp {
+
+constexpr int D = 128;
+constexpr int kHalf = 64;                       // keys per half-tile
+constexpr int kSlot = kHalf * D * 2;            // 16 KiB: 64 rows of 256 bytes
+constexpr int kMaxRoute = 2048;                 // route ids staged in LDS per team
+constexpr int kThreads = 512;
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(1))) const char gbl_char_t;
+
+// Slots hold 64 rows of 256 bytes; 16-byte chunk c of row r sits at chunk
+// c ^ (r & 15) for K and c ^ (4 r & 15) for V (conflict-free fragment reads).
+//
+// DMA of a half-tile: 16 instructions of 1 KiB, lane l of instruction n landing
+// at row 4 n + l / 16, physical chunk l % 16. Team wave tw issues n = tw + 4 i,
+// so n & 3 = tw is constant per wave and the logical chunk each lane fetches,
+// (l % 16) ^ ((4 n + l / 16) & 15) for K or (l % 16) ^ (4 (l / 16)) for V,
+// does not depend on i: one 32-bit lane offset serves all four instructions.
+__device__ __forceinline__ uint32_t dma_lane_off(int tw, int lane, bool is_v) {
+  const int x = lane >> 4, p = lane & 15;
+  const int c = is_v ? (p ^ (x << 2)) : (p ^ ((tw << 2) | x));
+  return static_cast<uint32_t>(x * 256 + c * 16) + static_cast<uint32_t>(tw * 1024);
+}
+// The same pointer, held in scalar registers (it is wave-uniform).
+__device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const bf16_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void dma_half(lds_char_t* slot, const bf16_t* src_any, uint32_t lane_off, int tw) {
+  gbl_char_t* sb = (gbl_char_t*)uniform_ptr(src_any);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // opaque 32-bit offset per load: keeps the scalar-base + 32-bit-offset
+    // addressing form (no 64-bit address arithmetic per load)
+    uint32_t off = lane_off + i * 4096;
+    asm volatile("" : "+v"(off));
+    __builtin_amdgcn_global_load_lds(sb + off, slot + (tw + 4 * i) * 1024, 16, 0, 0);
+  }
+}
+
+template <bool kRouted>
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
+  // Four slot arrays (K even/odd half-tile, V even/odd), each holding both
+  // teams' 16 KiB slots. With the half-tile loop unrolled by two every LDS
+  // access names its array, so the compiler can see that the DMA in flight
+  // targets other arrays than the reads of the current phase.
+  __shared__ __attribute__((aligned(1024))) char k_even[2 * kSlot];
+  __shared__ __attribute__((aligned(1024))) char k_odd[2 * kSlot];
+  __shared__ __attribute__((aligned(1024))) char v_even[2 * kSlot];
+  __shared__ __attribute__((aligned(1024))) char v_odd[2 * kSlot];
+  __shared__ int route_lds[2][kRouted ? kMaxRoute : 1];
+  __shared__ int pair_rows[2];
+  __shared__ int team_halves[2];
+
+  const int t = threadIdx.x, lane = t % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int team = wv >> 2, tw = wv & 3;
+  const int l32 = lane % 32, hh = lane / 32;
+  const int grp = lane / 16, gi = lane % 16;
+  const int N = a.N, M = a.M;
+  const int pairs = (N + 1) / 2;
+  const int G = (a.G / N) * pairs;
+  const int wg = xcd_remap(blockIdx.x, G);
+  const int h = wg / pairs, pr = wg % pairs;
+
+  // ---- this workgroup's two query blocks: rows of head h ranked by route
+  // length (longest first, ties by index); the pair is ranks 2 pr and 2 pr + 1.
+  if (t < 2) pair_rows[t] = -1;
+  __syncthreads();
+  for (int r = t; r < N; r += kThreads) {
+    int rank = r;
+    if (kRouted) {
+      const int* lens = a.route_len + static_cast<int64_t>(h) * N;
+      const int lr = min(max(lens[r], 0), a.L);
+      rank = 0;
+      for (int o = 0; o < N; ++o) {
+        const int lo = min(max(lens[o], 0), a.L);
+        rank += (lo > lr) || (lo == lr && o < r);
+      }
+    }
+    if (rank / 2 == pr) pair_rows[rank & 1] = r;
+  }
+  __syncthreads();
+  const int i = pair_rows[team];  // -1: this team has no block (odd N)
+
+  const bf16_t* kh = static_cast<const bf16_t*>(a.k) + h * a.ld_kv_h;
+  const bf16_t* vh = static_cast<const bf16_t*>(a.v) + h * a.ld_kv_h;
+  int rlen = 0, ncur = 0;
+  if (i >= 0) {
+    rlen = M;
+    if (kRouted) rlen = M == 0 ? 0 : min(max(a.route_len[static_cast<int64_t>(h) * N + i], 0), a.L);
+    ncur = (!kRouted || a.include_current) ? N : 0;
+  }
+  const int S = 2 * (rlen + ncur);     // half-tiles of this team's row
+  if (kRouted && i >= 0) {
+    const int32_t* route = a.route_ids + (static_cast<int64_t>(h) * N + i) * a.L;
+    for (int e = t - team * 256; e < rlen; e += 256) route_lds[team][e] = min(max(route[e], 0), M - 1);
+  }
+  if (tw == 0 && lane == 0) team_halves[team] = S;
+  __syncthreads();
+  // Phases: the lead team (0) runs MFMA(0), VALU(0), ..., MFMA(S), VALU(S);
+  // the other team starts one phase later. Both execute the same number of
+  // barriers: every wave of the workgroup must reach every barrier.
+  const int phases = max(2 * (team_halves[0] + 1), 1 + 2 * (team_halves[1] + 1));
+
+
+  // slot of half-tile parity P (a compile-time constant at every use)
+  auto kslot = [&](auto P) {
+    return (lds_char_t*)(decltype(P)::value ? k_odd : k_even) + team * kSlot;
+  };
+  auto vslot = [&](auto P) {
+    return (lds_char_t*)(decltype(P)::value ? v_odd : v_even) + team * kSlot;
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  const uint32_t koff_dma = dma_lane_off(tw, lane, false);
+  const uint32_t voff_dma = dma_lane_off(tw, lane, true);
+
+  const int qrow = (i >= 0 ? i : 0) * kBlock + tw * 32 + l32;  // this lane's query row
+  const bf16_t* qh = static_cast<const bf16_t*>(a.q) + h * a.ld_q_h;
+  bf16x8_t qf[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds)
+    qf[ds] = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const u32x4_t*>(qh + static_cast<int64_t>(qrow) * D + ds * 16 + hh * 8));
+
+  f32x16_t o_acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o_acc[db] = f32x16_t{};
+  f32x16_t s_acc[2];
+  bf16x8_t pf[4];
+  float m_ref = -INFINITY, l_run = 0.f;
+  const float sc = a.scale * 1.4426950408889634f;
+
+  // K fragment (row kb*32 + l32, logical chunk 2 ds + hh) sits at byte
+  //   kb*8192 + l32*256 + 16 (hh ^ z0) + 32 (ds ^ z1),  z = l32 & 15.
+  const int z = l32 & 15;
+  const int kbase = l32 * 256 + ((hh ^ (z & 1)) << 4);
+  const int kz1 = (z >> 1) << 5;
+  // V fragment (transpose read): row ks*16 + hh*4 + gi/4 (+8), logical chunk
+  // 4 db + 2 (grp & 1) + (gi & 3) / 2, half-chunk gi & 1.
+  int v_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int r = hh * 4 + gi / 4, c = 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1);
+    v_off[db] = r * 256 + ((c ^ ((r << 2) & 15)) << 4) + (gi & 1) * 8;
+  }
+
+  auto half_src = [&](const bf16_t* base, int j) {
+    const int jt = j >> 1;
+    int tile = jt < ncur ? M + jt : (kRouted ? route_lds[team][jt - ncur] : jt - ncur);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    return base + (static_cast<int64_t>(tile) * kBlock + (j & 1) * kHalf) * D;
+  };
+  // P: parity of j (Even / Odd), Q: the other parity
+  auto mfma_phase = [&](int j, auto P, auto Q) {
+    if (j > 0) {  // O += P(j-1) V(j-1)
+      lds_char_t* vs = vslot(Q);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          lds_char_t* vp = vs + v_off[db] + ks * 16 * 256;
+          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp));
+          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 8 * 256));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o_acc[db], 0, 0, 0);
+        }
+      }
+    }
+    if (j < S) {  // S(j) = K(j) Q^T
+      lds_char_t* ksl = kslot(P) + kbase;
+      const int z1 = kz1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s_acc[kb] = f32x16_t{};
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+          const bf16x8_t kf =
+              __builtin_bit_cast(bf16x8_t, *(const lds_u32x4_t*)(ksl + kb * 8192 + ((ds << 5) ^ z1)));
+          s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s_acc[kb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto valu_phase = [&](int j, auto P, auto Q) {
+    // refill the slots MFMA(j) just freed: K(j+2) into K(j)'s, V(j+1) into V(j-1)'s
+    const bool k_next = j + 2 < S, v_next = j + 1 < S;
+    if (k_next) dma_half(kslot(P), half_src(kh, j + 2), koff_dma, tw);
+    if (v_next) dma_half(vslot(Q), half_src(vh, j + 1), voff_dma, tw);
+    // softmax of S(j) against the lazy reference max
+    float m0 = s_acc[0][0], m1 = s_acc[1][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      m0 = fmaxf(m0, s_acc[0][r]);
+      m1 = fmaxf(m1, s_acc[1][r]);
+    }
+    float mx = fmaxf(m0, m1);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+    if (__ballot(mx > m_ref + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+    }
+    float ps[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x8_t lo, hi;
+      ps[2 * kb] = 0.f;
+      ps[2 * kb + 1] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        lo[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][r], sc, -m_ref));
+        hi[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][8 + r], sc, -m_ref));
+        ps[2 * kb] += lo[r];
+        ps[2 * kb + 1] += hi[r];
+      }
+      pf[2 * kb] = __builtin_convertvector(lo, bf16x8_t);
+      pf[2 * kb + 1] = __builtin_convertvector(hi, bf16x8_t);
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // K(j+1) and V(j), issued one VALU phase ago, must have landed before the
+    // barrier; the four or eight instructions just issued may still fly.
+    if (k_next && v_next)
+      tracked_wait_vmcnt<8>();
+    else if (k_next || v_next)
+      tracked_wait_vmcnt<4>();
+    else
+      tracked_wait_vm_all();
+  };
+
+  // prologue: K(0), K(1), V(0)
+  if (S > 0) {
+    dma_half(kslot(Even{}), half_src(kh, 0), koff_dma, tw);
+    dma_half(vslot(Even{}), half_src(vh, 0), voff_dma, tw);
+    if (S > 1) dma_half(kslot(Odd{}), half_src(kh, 1), koff_dma, tw);
+  }
+  tracked_wait_vm_all();
+  barrier_nofence();
+
+  int k = 0;
+  if (team == 1) {  // the second team starts one phase late
+    barrier_nofence();
+    ++k;
+  }
+  auto step = [&](int j, auto P, auto Q) {
+    mfma_phase(j, P, Q);
+    barrier_nofence();
+    if (j < S) valu_phase(j, P, Q);
+    barrier_nofence();
+  };
+  if (S > 0) {
+    for (int j = 0; j <= S; j += 2) {  // S is even
+      step(j, Even{}, Odd{});
+      if (j + 1 <= S) step(j + 1, Odd{}, Even{});
+      k += j + 1 <= S ? 4 : 2;
+    }
+  }
+  for (; k < phases; ++k) barrier_nofence();
+
+  if (i < 0) return;
+  // ---- normalise and store
+  bf16_t* orow = static_cast<bf16_t*>(a.o) + (static_cast<int64_t>(h) * N * kBlock + qrow) * D;
+  if (S == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<uint2*>(orow + db * 32 + g4 * 8 + hh * 4) = make_uint2(0u, 0u);
+    if (a.lse && hh == 0) a.lse[static_cast<int64_t>(h) * N * kBlock + qrow] = -INFINITY;
+    return;
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(o_acc[db][g4 * 4 + 0] * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16(o_acc[db][g4 * 4 + 1] * inv)) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(o_acc[db][g4 * 4 + 2] * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16(o_acc[db][g4 * 4 + 3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + db * 32 + g4 * 8 + hh * 4) = make_uint2(w0, w1);
+    }
+  }
+  if (a.lse && hh == 0)
+    a.lse[static_cast<int64_t>(h) * N * kBlock + qrow] = m_ref * 0.6931471805599453f + logf(l_tot);
+}
+
+}  // namespace pp
+
 // ---------------------------------------------------------------- fp32
 //
 // Plain VALU kernel for fp32 storage: one workgroup per (head, query block),
@@ -504,8 +829,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int D, bool kRouted>
 static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream) {
-  // d = 128: swizzled LDS tiles filled by direct DMA (routes of up to
-  // kMaxRouteLds tiles); otherwise padded tiles staged through registers.
+  // d = 128: the ping-pong kernel (routes of up to pp::kMaxRoute tiles), else
+  // swizzled tiles filled by direct DMA (up to kMaxRouteLds tiles); otherwise
+  // padded tiles staged through registers.
+  if (bf16 && D == 128 && (!kRouted || args.L <= pp::kMaxRoute)) {
+    const int pairs = (args.N + 1) / 2;
+    hipLaunchKernelGGL((pp::attn_kernel<kRouted>), dim3((args.G / args.N) * pairs), dim3(pp::kThreads),
+                       0, stream, args);
+    return hipGetLastError();
+  }
   const bool fast = D == 128 && (!kRouted || args.L <= kMaxRouteLds);
   if (bf16 && fast)
     hipLaunchKernelGGL((attn_bf16_kernel<D, kRouted, D == 128, D == 128>), dim3(args.G), dim3(256),

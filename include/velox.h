@@ -151,7 +151,10 @@ velox_status_t velox_route_select(const float* p, const float* g, const float* r
  *   o[h][i*128+a] = softmax_b( scale * q_a . k_b ) v_b
  * over the tokens b of the routed history tiles route_ids[h][i][0 .. len-1]
  * (len = clamp(route_len[h][i], 0, L)) followed, if include_current, by the
- * current chunk's tiles M .. M+N-1. Route ids outside [0, M) are skipped.
+ * current chunk's tiles M .. M+N-1. Route ids must be ascending, unique and
+ * in [0, M) (velox_route_select emits them so); the kernels do not check
+ * this, but clamp an id outside [0, M) into that range so that no load leaves
+ * the history (such an id then names the nearest valid tile).
  *   q        [H][N*128][d], head stride ld_q_h
  *   k, v     [H][>=(M+N)*128][d], head stride ld_kv_h
  *   o        [H][N*128][d] dtype dt, contiguous (output)

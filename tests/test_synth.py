@@ -1,0 +1,77 @@
+"""Synthetic-input generators: Gilbert rank map properties, chunk seams,
+coverage assignment and overlap ranges. CPU only."""
+
+import numpy as np
+import pytest
+
+import synth
+from synth.geometry import assign_coverage, obb_iou
+from synth.gilbert import chunk_block_coords, gilbert_cells
+
+
+@pytest.mark.parametrize("w,h", [(9, 4), (2, 2), (52, 29), (4, 3), (5, 5), (16, 16), (3, 7), (1, 6), (8, 1)])
+def test_gilbert_is_a_bijection_with_neighbour_steps(w, h):
+    cells = gilbert_cells(w, h)
+    assert len(cells) == w * h and len(set(cells)) == w * h
+    assert all(0 <= x < w and 0 <= y < h for x, y in cells)
+    assert cells[0] == (0, 0)
+    steps = [(abs(a[0] - b[0]), abs(a[1] - b[1])) for a, b in zip(cells, cells[1:])]
+    assert all(max(s) == 1 for s in steps)                 # always a grid neighbour
+    assert sum(1 for s in steps if s == (1, 1)) <= 1       # at most one diagonal step
+
+
+def test_chunk_seams_stay_adjacent():
+    co = chunk_block_coords(6, 4, 9)
+    assert co.shape == (6 * 36, 3)
+    for c in range(5):
+        last, first = co[c * 36 + 35], co[(c + 1) * 36]
+        assert first[0] == last[0] + 1 and first[1] == last[1] and first[2] == last[2]
+    # each chunk is a permutation of the 4x9 grid at its own t
+    for c in range(6):
+        cells = {(int(h), int(w)) for _, h, w in co[c * 36:(c + 1) * 36]}
+        assert cells == {(h, w) for h in range(4) for w in range(9)}
+
+
+def test_coverage_assignment():
+    rng = np.random.default_rng(0)
+    rho = assign_coverage(36, 0.6, rng)
+    assert rho.dtype == np.float32
+    assert int((rho >= np.float32(0.9)).sum()) == 22
+    assert rho.min() >= 0 and rho.max() < 1
+
+
+def test_obb_iou_identical_and_disjoint_boxes():
+    c = np.zeros((1, 3))
+    r = np.eye(3)[None]
+    e = np.ones((1, 3))
+    assert obb_iou(c, r, e, c, r, e)[0, 0] == pytest.approx(1.0)
+    assert obb_iou(c, r, e, c + 10, r, e)[0, 0] == 0.0
+    half = obb_iou(c, r, e, c + np.array([[1.0, 0, 0]]), r, e)[0, 0]
+    assert half == pytest.approx(1 / 3, abs=0.02)    # overlap 1/2 of each: IoU 1/3
+
+
+def test_workload_shapes_and_overlap_range():
+    w = synth.chunk48()
+    assert (w.H, w.d, w.N, w.M) == (40, 128, 36, 1692)
+    assert w.g.shape == (36, 1692) and w.coords.shape == (1728, 3)
+    assert 0.0 <= w.g.min() and w.g.max() <= 1.0
+    top = np.sort(w.g, axis=1)[:, -1]
+    assert 0.2 < np.median(top) < 0.9
+    assert w.route_cap == 176
+    t = synth.tiny()
+    assert t.coords.shape == (20, 3) and (t.g == 0).mean() > 0.5
+
+
+def test_make_qkv_is_seeded_and_offset():
+    w = synth.tiny()
+    q1, k1, v1 = synth.make_qkv(w)
+    q2, k2, v2 = synth.make_qkv(w)
+    assert (q1 == q2).all() and (k1 == k2).all() and (v1 == v2).all()
+    assert q1.shape == (2, 512, 64) and k1.shape == (2, 20 * 128, 64)
+    w2 = synth.wan13()
+    w2.H = 2
+    q, k, _ = synth.make_qkv(w2)
+    assert q.dtype.is_floating_point and str(q.dtype) == "torch.bfloat16"
+    # per-block offsets make block means spread well beyond the 1/sqrt(128) noise
+    km = k.float().view(2, -1, 128, 128).mean(2)
+    assert km.std().item() > 0.3
