@@ -61,8 +61,8 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a "
                          "known-size reference for HBM byte counters)")
-    ap.add_argument("--cpu-rows", type=int, default=480,
-                    help="query-block rows of the oracle's attention sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the sparse-attention part of the oracle sample")
     return ap.parse_args()
 
 
@@ -79,7 +79,7 @@ def unique_tile_count(ids, lens, N, M):
     return total
 
 
-def cpu_baseline(wl, q, k, v, p, ids, lens, rows_n):
+def cpu_baseline(wl, q, k, v, p, ids, lens, seconds, max_rows=4096):
     """Oracle timed on a bounded sample, extrapolated to one whole call."""
     import numpy as np
     import torch
@@ -110,12 +110,17 @@ def cpu_baseline(wl, q, k, v, p, ids, lens, rows_n):
         oracle.route_row(p_np[0, i], wl.g[i], wl.rho[i], wl.params, wl.M, wl.coords, i)
     t_route = time.perf_counter() - t0
 
-    rows = [(int(rng.integers(0, 2)), int(rng.integers(0, wl.N))) for _ in range(rows_n)]
+    # random (head, block) rows of the two sampled heads, drawn with replacement
+    # until the time budget is spent (at least 8, at most max_rows)
     t0 = time.perf_counter()
-    for h, i in rows:
+    done = 0
+    while done < max_rows and (done < 8 or time.perf_counter() - t0 < seconds):
+        h, i = int(rng.integers(0, 2)), int(rng.integers(0, wl.N))
         route = ids_np[heads[h], i, : lens_np[heads[h], i]].tolist()
         oracle.sparse_attention_block(qn, kn, vn, wl.scale, h, i, route, wl.M, wl.N)
+        done += 1
     t_attn = time.perf_counter() - t0
+    rows_n = done
     n_rows = wl.H * wl.N
     total_s = wl.H * t_imp + wl.H * t_route + n_rows / rows_n * t_attn
     return {
@@ -124,7 +129,8 @@ def cpu_baseline(wl, q, k, v, p, ids, lens, rows_n):
         "cores": int(cores),
         "kind": "oracle",
         "sample": (f"importance of 1 head, routes of the 36 rows of 1 head, sparse attention of "
-                   f"{rows_n} random (head, block) rows; scaled to 40 heads x 36 rows "
+                   f"{rows_n} (head, block) rows drawn with replacement from heads 0-1; scaled to "
+                   f"{wl.H} heads x {wl.N} rows "
                    f"(measured {t_imp + t_route + t_attn:.1f} s of CPU time)"),
     }
 
@@ -265,7 +271,7 @@ def main():
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
             "traffic_note": None,
-            "kernel": "attn_bf16_kernel<128, routed>",
+            "kernel": "velox::pp::attn_kernel<true> (routed, d 128, bf16)",
             "hbm_unique_bytes": uniq_bytes,
             "hbm_frac_unique": round(uniq_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
@@ -280,7 +286,7 @@ def main():
             f"write {tr['write_bytes'] / 1e9:.3f} GB")
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, p, ids, lens, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, p, ids, lens, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
