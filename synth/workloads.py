@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .geometry import assign_coverage, obb_iou, slab_obbs
+from .geometry import _token_depths, assign_coverage, mc_overlap, pack_obbs, slab_obbs, token_points
 from .gilbert import chunk_block_coords
 
 BLOCK = 128          # tokens per block = attention tile (b_tok)
@@ -66,6 +66,10 @@ class Workload:
     rho: np.ndarray              # [N] float32 coverage
     kv_blocks: int = 0           # KV capacity in blocks (>= M + N)
     notes: dict = field(default_factory=dict)
+    # slab scene behind g (None for hand-made overlaps): "obb_hist" [M,16] and
+    # "obb_query" [N,16] packed float32 OBB records, "query_pts" [N,128,3]
+    # float32 token world points (NaN = no depth)
+    scene: dict | None = None
 
     @property
     def scale(self) -> float:
@@ -80,11 +84,16 @@ class Workload:
 
 
 def _slab_geometry(coords: np.ndarray, M: int, N: int, seed: int):
+    """Slab scene of M history + N query blocks; g by seeded Monte Carlo IoU."""
     rng = np.random.default_rng(seed)
     chunk = coords[:, 0]
-    c, ax, hf = slab_obbs(coords, chunk, GRID_H, GRID_W, rng)
-    g = obb_iou(c[M:], ax[M:], hf[M:], c[:M], ax[:M], hf[:M])
-    return g.astype(np.float32), rng
+    depths = _token_depths(rng, M + N)
+    c, ax, hf = slab_obbs(coords, chunk, GRID_H, GRID_W, rng, depths=depths)
+    pts = token_points(coords[M:], chunk[M:], GRID_H, GRID_W, depths[M:], rng)
+    g = mc_overlap(c[M:], ax[M:], hf[M:], c[:M], ax[:M], hf[:M], rng)
+    scene = {"obb_hist": pack_obbs(c[:M], ax[:M], hf[:M]),
+             "obb_query": pack_obbs(c[M:], ax[M:], hf[M:]), "query_pts": pts}
+    return g.astype(np.float32), rng, scene
 
 
 def tiny() -> Workload:
@@ -103,11 +112,11 @@ def wan13() -> Workload:
     """Wan-1.3B-like layer: 12 heads, d = 128, bf16, 36 query, 143 history blocks."""
     N, M = 36, 143
     coords = chunk_block_coords(5, GRID_H, GRID_W, first_id_offset=5 * 36 - (M + N))
-    g, rng = _slab_geometry(coords, M, N, seed=1)
+    g, rng, scene = _slab_geometry(coords, M, N, seed=1)
     rho = assign_coverage(N, 0.6, rng)
     prm = RouteParams()
     return Workload("wan13", 12, 128, "bf16", N, M, 1, 0.5, prm, coords, g, rho,
-                    kv_blocks=M + N)
+                    kv_blocks=M + N, scene=scene)
 
 
 def chunk48(covered_fraction: float = 0.6, seed: int = 48, name: str = "chunk48",
@@ -116,11 +125,11 @@ def chunk48(covered_fraction: float = 0.6, seed: int = 48, name: str = "chunk48"
     N = CHUNK_BLOCKS
     M = 47 * CHUNK_BLOCKS
     coords = chunk_block_coords(48, GRID_H, GRID_W)
-    g, rng = _slab_geometry(coords, M, N, seed=seed)
+    g, rng, scene = _slab_geometry(coords, M, N, seed=seed)
     rho = assign_coverage(N, covered_fraction, rng)
     prm = RouteParams(n_prev=CHUNK_BLOCKS, neigh26=1)
     return Workload(name, heads, 128, "bf16", N, M, seed, 0.5, prm, coords, g, rho,
-                    kv_blocks=M + N, notes={"covered_fraction": covered_fraction})
+                    kv_blocks=M + N, notes={"covered_fraction": covered_fraction}, scene=scene)
 
 
 def sweep(covered_fraction: float) -> Workload:
@@ -135,13 +144,13 @@ def trace_chunk(chunk: int, layer: int, heads: int = 40) -> Workload:
     M = CHUNK_BLOCKS * (chunk - 1)
     coords = chunk_block_coords(chunk, GRID_H, GRID_W)
     if M > 0:
-        g, rng = _slab_geometry(coords, M, N, seed=1000 + layer)
+        g, rng, scene = _slab_geometry(coords, M, N, seed=1000 + layer)
     else:
-        g, rng = np.zeros((N, 0), np.float32), np.random.default_rng(1000 + layer)
+        g, rng, scene = np.zeros((N, 0), np.float32), np.random.default_rng(1000 + layer), None
     rho = assign_coverage(N, 0.6, rng)
     prm = RouteParams(n_prev=min(CHUNK_BLOCKS, M), neigh26=1)
     return Workload(f"trace_c{chunk}_l{layer}", heads, 128, "bf16", N, M, 1000 + layer,
-                    0.5, prm, coords, g, rho, kv_blocks=M + N)
+                    0.5, prm, coords, g, rho, kv_blocks=M + N, scene=scene)
 
 
 def make_qkv(wl: Workload, device="cpu", kv_blocks: int | None = None):

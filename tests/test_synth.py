@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from synth.geometry import assign_coverage, obb_iou
+from synth.geometry import assign_coverage, mc_overlap
 from synth.gilbert import chunk_block_coords, gilbert_cells
 
 
@@ -40,14 +40,31 @@ def test_coverage_assignment():
     assert rho.min() >= 0 and rho.max() < 1
 
 
-def test_obb_iou_identical_and_disjoint_boxes():
+def test_mc_overlap_identical_and_disjoint_boxes():
     c = np.zeros((1, 3))
     r = np.eye(3)[None]
     e = np.ones((1, 3))
-    assert obb_iou(c, r, e, c, r, e)[0, 0] == pytest.approx(1.0)
-    assert obb_iou(c, r, e, c + 10, r, e)[0, 0] == 0.0
-    half = obb_iou(c, r, e, c + np.array([[1.0, 0, 0]]), r, e)[0, 0]
+    rng = np.random.default_rng(0)
+    assert mc_overlap(c, r, e, c, r, e, rng)[0, 0] == pytest.approx(1.0)
+    assert mc_overlap(c, r, e, c + 10, r, e, rng)[0, 0] == 0.0
+    half = mc_overlap(c, r, e, c + np.array([[1.0, 0, 0]]), r, e, rng, samples=20000)[0, 0]
     assert half == pytest.approx(1 / 3, abs=0.02)    # overlap 1/2 of each: IoU 1/3
+
+
+def test_scene_records_and_points():
+    w = synth.wan13()
+    sc = w.scene
+    assert sc["obb_hist"].shape == (143, 16) and sc["obb_query"].shape == (36, 16)
+    assert sc["query_pts"].shape == (36, 128, 3) and sc["query_pts"].dtype == np.float32
+    assert (sc["obb_hist"][:, 3:6] > 0).all()
+    R = sc["obb_hist"][:, 6:15].reshape(-1, 3, 3).astype(float)
+    assert np.allclose(R @ R.transpose(0, 2, 1), np.eye(3), atol=1e-5)
+    # query token points lie on their own block's slab depth range
+    c, e, Rq = sc["obb_query"][:, 0:3], sc["obb_query"][:, 3:6], sc["obb_query"][:, 6:15].reshape(-1, 3, 3)
+    loc = np.einsum("npk,nkj->npj", sc["query_pts"].astype(float) - c[:, None], Rq)
+    ok = ~np.isnan(loc).any(-1)
+    frac = (np.abs(loc[..., 2]) <= e[:, None, 2] + 1e-4)[ok].mean()
+    assert 0.7 < frac < 0.9                        # the 10/90 interval holds ~80%
 
 
 def test_workload_shapes_and_overlap_range():
