@@ -218,6 +218,28 @@ def main():
     torch.cuda.synchronize()
     dense_ms = ds.elapsed_time(de) / args.dense_steps
 
+    # geometry scorer on the same scene (once per chunk, not per layer: reported
+    # beside the step, not in it)
+    sc = wl.scene
+    qo = torch.from_numpy(sc["obb_query"]).to(dev)
+    ho = torch.from_numpy(sc["obb_hist"]).to(dev)
+    qp = torch.from_numpy(sc["query_pts"]).to(dev)
+    g_out = velox.slab_overlap(qo, ho, lattice=8)
+    rho_out, mask_out = velox.slab_coverage(qp, ho)
+    torch.cuda.synchronize()
+    geo_ms = {}
+    for name, fn in (("slab_overlap", lambda: velox.slab_overlap(qo, ho, lattice=8, out=g_out)),
+                     ("slab_coverage", lambda: velox.slab_coverage(qp, ho, rho=rho_out,
+                                                                   token_mask=mask_out))):
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(20):
+            fn()
+        ge.record()
+        torch.cuda.synchronize()
+        geo_ms[name] = round(gs.elapsed_time(ge) / 20, 4)
+    log(f"geometry: overlap {geo_ms['slab_overlap']:.4f} ms, coverage {geo_ms['slab_coverage']:.4f} ms")
+
     lens_np = lens.cpu().numpy()
     tiles = int((lens_np + wl.N).sum())
     blk = 128
@@ -261,6 +283,8 @@ def main():
         "dense_ms": round(dense_ms, 4),
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
         "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
+        "geometry_ms": geo_ms,
+        "geometry_point_tests": {"slab_overlap": wl.N * wl.M * 512, "slab_coverage": wl.N * 128 * wl.M},
         "tiles_visited": tiles,
         "history_flop_share": round(flop_hist / flop, 4),
         "roofline": {

@@ -2,7 +2,8 @@
 
 Thin PyTorch binding of libvelox.so: every function here only checks tensor
 metadata, marshals pointers and the current HIP stream, and calls the C ABI of
-include/velox.h. All computation runs in the library's HIP kernels.
+include/velox.h and include/velox_geometry.h. All computation runs in the
+library's HIP kernels.
 
 Layouts (row-major, token rows contiguous):
     q            [H][N*128][d]          bf16 or fp32
@@ -12,6 +13,8 @@ Layouts (row-major, token rows contiguous):
     g            [N][M] fp32, rho [N] fp32, coord [M+N][3] int32
     route_ids    [H][N][L] int32, route_len [H][N] int32
     o            [H][N*128][d]          dtype of q;  lse [H][N*128] fp32
+    obb records  [n][16] fp32 (centre, half-extents, axes row-major, unused)
+    q_pts        [N][128][3] fp32 token world points (NaN = no depth)
 """
 
 from __future__ import annotations
@@ -23,7 +26,8 @@ from . import _lib
 from ._lib import VELOX_BLOCK, VeloxError
 
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
-           "route_bound", "sparse_attn", "dense_attn", "library_path"]
+           "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
+           "library_path"]
 
 
 def library_path() -> str:
@@ -201,3 +205,53 @@ def dense_attn(q, k, v, M: int, scale: float | None = None, out=None, lse=None,
                                     ctypes.c_float(scale), out.data_ptr(),
                                     lse.data_ptr() if lse is not None else None, _stream(q)))
     return (out, lse) if want_lse or lse is not None else out
+
+
+def _obb(t, name):
+    torch = _torch()
+    if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != _lib.VELOX_OBB_WORDS:
+        raise ValueError(f"{name} must be float32 [n][{_lib.VELOX_OBB_WORDS}]")
+    _contig(t, name)
+
+
+def slab_overlap(q_obb, h_obb, lattice: int = 8, out=None):
+    """g [N][M] fp32: lattice-approximated IoU of query and history slab boxes."""
+    torch = _torch()
+    _require_cuda(q_obb, h_obb)
+    _obb(q_obb, "q_obb")
+    _obb(h_obb, "h_obb")
+    N, M = q_obb.shape[0], h_obb.shape[0]
+    if out is None:
+        out = torch.empty(N, M, dtype=torch.float32, device=q_obb.device)
+    _require_cuda(out)
+    _contig(out, "out")
+    if out.shape != (N, M) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [N][M]")
+    lib = _lib.load()
+    _lib.check(lib.velox_slab_overlap(q_obb.data_ptr(), h_obb.data_ptr(), N, M, lattice,
+                                      out.data_ptr(), _stream(q_obb)))
+    return out
+
+
+def slab_coverage(q_pts, h_obb, rho=None, token_mask=None):
+    """(rho [N] fp32, token_mask [N][4] int32 bit masks) of query token points."""
+    torch = _torch()
+    _require_cuda(q_pts, h_obb)
+    _obb(h_obb, "h_obb")
+    if q_pts.dtype != torch.float32 or q_pts.dim() != 3 or q_pts.shape[1:] != (VELOX_BLOCK, 3):
+        raise ValueError("q_pts must be float32 [N][128][3]")
+    _contig(q_pts, "q_pts")
+    N, M = q_pts.shape[0], h_obb.shape[0]
+    if rho is None:
+        rho = torch.empty(N, dtype=torch.float32, device=q_pts.device)
+    if token_mask is None:
+        token_mask = torch.empty(N, 4, dtype=torch.int32, device=q_pts.device)
+    _require_cuda(rho, token_mask)
+    _contig(rho, "rho")
+    _contig(token_mask, "token_mask")
+    if rho.shape != (N,) or token_mask.shape != (N, 4) or token_mask.element_size() != 4:
+        raise ValueError("rho must be [N] and token_mask [N][4] of 32-bit words")
+    lib = _lib.load()
+    _lib.check(lib.velox_slab_coverage(q_pts.data_ptr(), h_obb.data_ptr(), N, M,
+                                       token_mask.data_ptr(), rho.data_ptr(), _stream(q_pts)))
+    return rho, token_mask

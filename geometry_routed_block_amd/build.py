@@ -3,8 +3,9 @@
     python -m geometry_routed_block_amd.build        # or build() from Python
 
 Every translation unit is compiled with packed-fp32 instruction selection
-disabled. The router unit is additionally compiled with -ffp-contract=off:
-its float32 fusion must round each operation separately.
+disabled. The router and geometry units are additionally compiled with
+-ffp-contract=off: their float32 decisions must round each operation
+separately.
 """
 
 from __future__ import annotations
@@ -26,6 +27,7 @@ COMMON = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
 UNITS = [
     ("velox_route.hip", ["-ffp-contract=off"]),
     ("velox_attn.hip", []),
+    ("velox_geom.hip", ["-ffp-contract=off"]),
     ("velox_api.cpp", ["-x", "hip"]),
 ]
 

@@ -1,6 +1,6 @@
 // C ABI of libvelox: argument validation, error reporting and dispatch to the
 // kernel launchers. Declarations, layouts and the cited definitions of each
-// operation are in include/velox.h.
+// operation are in include/velox.h and include/velox_geometry.h.
 
 #include <hip/hip_runtime.h>
 
@@ -10,6 +10,7 @@
 #include <string>
 
 #include "../../include/velox.h"
+#include "../../include/velox_geometry.h"
 #include "velox_launch.hpp"
 
 namespace {
@@ -72,6 +73,14 @@ velox_status_t check_attn(const void* q, const void* k, const void* v, velox_dty
 
 }  // namespace
 
+static int64_t elem_bytes(velox_dtype_t dt) { return dt == VELOX_BF16 ? 2 : 4; }
+
+static velox_status_t check_geometry_sizes(int N, int M) {
+  REQUIRE(N >= 0 && M >= 0, "N and M must be >= 0 (got N=%d M=%d)", N, M);
+  REQUIRE(N <= 65535, "N=%d exceeds 65535", N);
+  return VELOX_OK;
+}
+
 extern "C" {
 
 const char* velox_last_error(void) { return g_last_error.c_str(); }
@@ -87,6 +96,8 @@ velox_status_t velox_block_mean(const void* x, velox_dtype_t dt, int64_t ld_x_h,
   REQUIRE(x && xbar, "x and xbar must be non-NULL");
   REQUIRE(ld_x_h >= static_cast<int64_t>(nblk) * VELOX_BLOCK * d, "ld_x_h too small");
   REQUIRE(ld_bar_h >= static_cast<int64_t>(nblk) * d, "ld_bar_h too small");
+  REQUIRE(reinterpret_cast<uintptr_t>(x) % 16 == 0 && (ld_x_h * elem_bytes(dt)) % 16 == 0,
+          "x and its head stride must be 16-byte aligned");
   return launched(velox::launch_block_mean(x, dt == VELOX_BF16, ld_x_h, H, nblk, d, xbar, ld_bar_h,
                                            static_cast<hipStream_t>(stream)),
                   "velox_block_mean");
@@ -102,6 +113,10 @@ velox_status_t velox_route_scores(const void* q, velox_dtype_t dt, int64_t ld_q_
   REQUIRE(ld_q_h >= static_cast<int64_t>(N) * VELOX_BLOCK * d, "ld_q_h too small");
   REQUIRE(ld_kbar_h >= static_cast<int64_t>(M) * d, "ld_kbar_h too small");
   REQUIRE(std::isfinite(scale), "scale must be finite");
+  REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && (ld_q_h * elem_bytes(dt)) % 16 == 0,
+          "q and its head stride must be 16-byte aligned");
+  REQUIRE(reinterpret_cast<uintptr_t>(kbar) % 16 == 0 && ld_kbar_h % 4 == 0,
+          "kbar and its head stride must be 16-byte aligned");
   if (velox::route_scores_lds_bytes(1, M, d) > velox::kMaxLdsBytes)
     return fail(VELOX_ERR_UNSUPPORTED, "M=%d too large for route_scores", M);
   return launched(velox::launch_route_scores(q, dt == VELOX_BF16, ld_q_h, kbar, ld_kbar_h, H, N, M, d,
@@ -165,6 +180,31 @@ velox_status_t velox_dense_attn(const void* q, const void* k, const void* v, vel
   velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
                       nullptr, nullptr, 0, 1, o, lse};
   return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), "velox_dense_attn");
+}
+
+velox_status_t velox_slab_overlap(const float* q_obb, const float* h_obb, int N, int M,
+                                  int lattice, float* g, void* stream) {
+  velox_status_t st = check_geometry_sizes(N, M);
+  if (st != VELOX_OK) return st;
+  REQUIRE(lattice >= 1 && lattice <= VELOX_MAX_LATTICE, "lattice must be in [1, %d] (got %d)",
+          VELOX_MAX_LATTICE, lattice);
+  if (N == 0 || M == 0) return VELOX_OK;
+  REQUIRE(q_obb && h_obb && g, "q_obb, h_obb and g must be non-NULL");
+  return launched(velox::launch_slab_overlap(q_obb, h_obb, N, M, lattice, g,
+                                             static_cast<hipStream_t>(stream)),
+                  "velox_slab_overlap");
+}
+
+velox_status_t velox_slab_coverage(const float* q_pts, const float* h_obb, int N, int M,
+                                   uint32_t* token_mask, float* rho, void* stream) {
+  velox_status_t st = check_geometry_sizes(N, M);
+  if (st != VELOX_OK) return st;
+  if (N == 0) return VELOX_OK;
+  REQUIRE(token_mask && rho, "token_mask and rho must be non-NULL");
+  REQUIRE(M == 0 || (q_pts && h_obb), "q_pts and h_obb must be non-NULL when M > 0");
+  return launched(velox::launch_slab_coverage(q_pts, h_obb, N, M, token_mask, rho,
+                                              static_cast<hipStream_t>(stream)),
+                  "velox_slab_coverage");
 }
 
 }  // extern "C"

@@ -43,5 +43,9 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
                                const int32_t* coord, int H, int N, int M, const RouteConfig& cfg,
                                int L, int32_t* route_ids, int32_t* route_len, hipStream_t stream);
 hipError_t launch_attention(const AttnConfig& cfg, hipStream_t stream);
+hipError_t launch_slab_overlap(const float* q_obb, const float* h_obb, int N, int M, int n,
+                               float* g, hipStream_t stream);
+hipError_t launch_slab_coverage(const float* q_pts, const float* h_obb, int N, int M,
+                                uint32_t* mask, float* rho, hipStream_t stream);
 
 }  // namespace velox

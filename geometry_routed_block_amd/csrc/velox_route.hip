@@ -71,22 +71,44 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // ---------------------------------------------------------------- block means
 
+// One workgroup (256 threads) per (block, head). Each thread reads 16-byte
+// vectors of one column group from 128 / (256 / vpr) rows (vpr = vectors per
+// row), then the row groups are summed through LDS. Summation order: per
+// thread over its rows in ascending order, then over row groups in ascending
+// order.
 template <typename T>
 __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x, int64_t ld_x_h,
                                                          int d, float* __restrict__ xbar,
                                                          int64_t ld_bar_h) {
-  __shared__ float part[256];
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  __shared__ float part[256 * V];
   const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int parts = 256 / d;  // d in {64, 128}
-  const int c = t % d, s = t / d;
-  const T* src = x + h * ld_x_h + static_cast<int64_t>(b) * kBlock * d;
-  float acc = 0.f;
-  for (int a = s; a < kBlock; a += parts) acc += load_f32(src + a * d + c);
-  part[t] = acc;
+  const int vpr = d / V, groups = 256 / vpr;
+  const int cv = t % vpr, g = t / vpr;
+  const T* src = x + h * ld_x_h + static_cast<int64_t>(b) * kBlock * d + cv * V;
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  for (int a = g; a < kBlock; a += groups) {
+    const uint4 u = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(a) * d);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (V == 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(w[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(w[j] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(w[j]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) part[g * d + cv * V + e] = acc[e];
   __syncthreads();
   if (t < d) {
     float tot = 0.f;
-    for (int j = 0; j < parts; ++j) tot += part[j * d + t];
+    for (int j = 0; j < groups; ++j) tot += part[j * d + t];
     xbar[h * ld_bar_h + static_cast<int64_t>(b) * d + t] = tot * (1.0f / kBlock);
   }
 }

@@ -92,7 +92,8 @@ int velox_version(void);
  * The per-block means of the pages' importance ([digest] Method steps, step 4,
  * eq. 9: mean query and mean key of a block). Used to fill the key-mean cache
  * when a chunk joins the history (a finished chunk's keys never change).
- *   x     [H][nblk*128][d], dtype dt, head stride ld_x_h (>= nblk*128*d)
+ *   x     [H][nblk*128][d], dtype dt, head stride ld_x_h (>= nblk*128*d);
+ *         x and ld_x_h in bytes must be multiples of 16
  *   xbar  [H][nblk][d] fp32, head stride ld_bar_h (>= nblk*d)
  * nblk >= 0 (0: no-op).
  */
@@ -107,6 +108,7 @@ velox_status_t velox_block_mean(const void* x, velox_dtype_t dt, int64_t ld_x_h,
  * with qbar the block means of q computed inside the call (fp32 accumulation).
  *   q     [H][N*128][d], dtype dt, head stride ld_q_h (>= N*128*d)
  *   kbar  [H][>=M][d] fp32 key-mean cache, head stride ld_kbar_h (>= M*d)
+ *         q, kbar and both head strides in bytes must be multiples of 16
  *   p     [H][N][M] fp32, contiguous (output)
  * scale is normally 1/sqrt(d). M == 0 writes nothing.
  */

@@ -113,24 +113,39 @@ def overlap_pair(a, b, n: int = 8) -> np.float32:
 
 
 def slab_overlap(q_obb, h_obb, n: int = 8) -> np.ndarray:
-    """g [N][M] float32 for query boxes [N,16] against history boxes [M,16]."""
+    """g [N][M] float32 for query boxes [N,16] against history boxes [M,16].
+
+    Element for element the arithmetic of overlap_pair; the inside test runs
+    for all history boxes of a row at once (numpy broadcasting).
+    """
     q_obb = np.asarray(q_obb, dtype=f32)
     h_obb = np.asarray(h_obb, dtype=f32)
-    g = np.zeros((q_obb.shape[0], h_obb.shape[0]), dtype=f32)
-    for i in range(q_obb.shape[0]):
+    N, M = q_obb.shape[0], h_obb.shape[0]
+    g = np.zeros((N, M), dtype=f32)
+    if M == 0:
+        return g
+    hc, he, hR = h_obb[:, 0:3], h_obb[:, 3:6], h_obb[:, 6:15].reshape(M, 3, 3)
+    hvalid = (he > 0).all(axis=1)
+    hvol = np.array([obb_volume(rec) for rec in h_obb], dtype=f32)
+    for i in range(N):
         if not obb_valid(q_obb[i]):
             continue
-        pts = lattice_points(q_obb[i], n)
+        pts = lattice_points(q_obb[i], n)                               # [P,3]
+        d = (pts[None, :, :] - hc[:, None, :]).astype(f32)              # [M,P,3]
+        ok = np.ones(d.shape[:2], dtype=bool)
+        for j in range(3):
+            l = (hR[:, 0, j, None] * d[:, :, 0]).astype(f32)
+            l = (l + (hR[:, 1, j, None] * d[:, :, 1]).astype(f32)).astype(f32)
+            l = (l + (hR[:, 2, j, None] * d[:, :, 2]).astype(f32)).astype(f32)
+            ok &= np.abs(l) <= he[:, j, None]
+        count = ok.sum(axis=1)
         va = obb_volume(q_obb[i])
-        for r in range(h_obb.shape[0]):
-            if not obb_valid(h_obb[r]):
+        for r in range(M):
+            if not hvalid[r] or count[r] == 0:
                 continue
-            count = int(inside_obb(pts, h_obb[r]).sum())
-            if count == 0:
-                continue
-            frac = f32(f32(count) / f32(n * n * n))
+            frac = f32(f32(int(count[r])) / f32(n * n * n))
             inter = f32(va * frac)
-            g[i, r] = f32(inter / f32(f32(va + obb_volume(h_obb[r])) - inter))
+            g[i, r] = f32(inter / f32(f32(va + hvol[r]) - inter))
     return g
 
 

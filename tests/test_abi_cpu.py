@@ -11,13 +11,14 @@ import pytest
 from geometry_routed_block_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "velox.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 BAD = 0x1000  # a non-NULL pointer value that validation must reject before use
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"\b(velox_[a-z_0-9]+)\s*\(", text)))
 
 
@@ -112,3 +113,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_geometry_validation(lib):
+    ov, cv = lib.velox_slab_overlap, lib.velox_slab_coverage
+    assert ov(BAD, BAD, 4, 16, 0, BAD, None) == _lib.VELOX_ERR_INVALID          # lattice 0
+    assert b"lattice" in lib.velox_last_error()
+    assert ov(BAD, BAD, 4, 16, 17, BAD, None) == _lib.VELOX_ERR_INVALID         # lattice 17
+    assert ov(BAD, BAD, -1, 16, 8, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert ov(BAD, BAD, 70000, 16, 8, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert ov(None, BAD, 4, 16, 8, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert ov(None, None, 0, 16, 8, None, None) == _lib.VELOX_OK                # N = 0: no-op
+    assert ov(None, None, 4, 0, 8, None, None) == _lib.VELOX_OK                 # M = 0: no-op
+    assert cv(BAD, BAD, 4, 16, None, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert cv(None, BAD, 4, 16, BAD, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert cv(BAD, BAD, 4, -2, BAD, BAD, None) == _lib.VELOX_ERR_INVALID
+    assert cv(None, None, 0, 5, None, None, None) == _lib.VELOX_OK
