@@ -3,11 +3,11 @@
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library."""
 
-from . import geometry
+from . import geometry, layout
 from .velox_oracle import (BLOCK, attention_block, block_means, dense_attention_block,
                            fixed_mass, fused_weights, ghat, importance, route_row, routes,
                            sparse_attention_block)
 
-__all__ = ["BLOCK", "geometry", "attention_block", "block_means", "dense_attention_block", "fixed_mass",
+__all__ = ["BLOCK", "geometry", "layout", "attention_block", "block_means", "dense_attention_block", "fixed_mass",
            "fused_weights", "ghat", "importance", "route_row", "routes",
            "sparse_attention_block"]

@@ -24,7 +24,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .geometry import _token_depths, assign_coverage, mc_overlap, pack_obbs, slab_obbs, token_points
-from .gilbert import chunk_block_coords
+from .blockgrid import chunk_block_coords
 
 BLOCK = 128          # tokens per block = attention tile (b_tok)
 CHUNK_BLOCKS = 36    # blocks per generated chunk
