@@ -240,6 +240,27 @@ def main():
         geo_ms[name] = round(gs.elapsed_time(ge) / 20, 4)
     log(f"geometry: overlap {geo_ms['slab_overlap']:.4f} ms, coverage {geo_ms['slab_coverage']:.4f} ms")
 
+    # KV append of one chunk in global order (once per chunk per layer, at
+    # model QKV time: reported beside the step). 3 latent frames of 32 x 48
+    # tokens = the 36 blocks of a chunk, written over the current chunk's rows
+    # after every timing above is done.
+    Tl, Hl, Wl = 3, 32, 48
+    k_new = torch.randn(wl.H, Tl * Hl * Wl, wl.d, device=dev).to(k.dtype)
+    v_new = torch.randn_like(k_new)
+    kb_cache = torch.zeros(wl.H, wl.M + wl.N, wl.d, device=dev)
+    cells = torch.from_numpy(velox.gilbert_curve(Wl, Hl)).to(dev)
+    velox.kv_append(k_new, v_new, Tl, Hl, Wl, 47, cells, k, v, wl.M * 128, kbar=kb_cache)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(20):
+        velox.kv_append(k_new, v_new, Tl, Hl, Wl, 47, cells, k, v, wl.M * 128, kbar=kb_cache)
+    a1.record()
+    torch.cuda.synchronize()
+    append_ms = a0.elapsed_time(a1) / 20
+    append_bytes = 4 * k_new.numel() * k_new.element_size() + wl.H * wl.N * wl.d * 4
+    log(f"kv_append: {append_ms:.4f} ms, {append_bytes / append_ms / 1e6:.0f} GB/s")
+
     lens_np = lens.cpu().numpy()
     tiles = int((lens_np + wl.N).sum())
     blk = 128
@@ -284,6 +305,9 @@ def main():
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
         "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
         "geometry_ms": geo_ms,
+        "kv_append": {"ms": round(append_ms, 4), "bytes": append_bytes,
+                      "gbps": round(append_bytes / append_ms / 1e6, 1),
+                      "frac_hbm": round(append_bytes / append_ms / 1e6 / PEAK_HBM_GBPS, 4)},
         "geometry_point_tests": {"slab_overlap": wl.N * wl.M * 512, "slab_coverage": wl.N * 128 * wl.M},
         "tiles_visited": tiles,
         "history_flop_share": round(flop_hist / flop, 4),

@@ -2,8 +2,9 @@
 
 Thin PyTorch binding of libvelox.so: every function here only checks tensor
 metadata, marshals pointers and the current HIP stream, and calls the C ABI of
-include/velox.h and include/velox_geometry.h. All computation runs in the
-library's HIP kernels.
+include/velox.h, include/velox_geometry.h and include/velox_layout.h. All
+computation runs in the library's HIP kernels (the curve of velox_gilbert_curve
+is computed by the library's host code).
 
 Layouts (row-major, token rows contiguous):
     q            [H][N*128][d]          bf16 or fp32
@@ -27,7 +28,7 @@ from ._lib import VELOX_BLOCK, VeloxError
 
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
            "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
-           "library_path"]
+           "gilbert_curve", "kv_append", "library_path"]
 
 
 def library_path() -> str:
@@ -255,3 +256,41 @@ def slab_coverage(q_pts, h_obb, rho=None, token_mask=None):
     _lib.check(lib.velox_slab_coverage(q_pts.data_ptr(), h_obb.data_ptr(), N, M,
                                        token_mask.data_ptr(), rho.data_ptr(), _stream(q_pts)))
     return rho, token_mask
+
+
+def gilbert_curve(width: int, height: int):
+    """numpy int32 [width*height]: y*width + x of the k-th cell along the curve."""
+    import numpy as np
+    cells = np.empty(width * height, dtype=np.int32)
+    lib = _lib.load()
+    _lib.check(lib.velox_gilbert_curve(width, height, cells.ctypes.data))
+    return cells
+
+
+def kv_append(k_new, v_new, T: int, height: int, width: int, chunk_index: int, cells,
+              k_cache, v_cache, token_offset: int, kbar=None):
+    """Write one chunk (THW-linear [H][T*height*width][d]) into the caches in
+    global order at token_offset; refresh kbar for its blocks when given."""
+    torch = _torch()
+    _require_cuda(k_new, v_new, cells, k_cache, v_cache, kbar)
+    if k_new.dtype != v_new.dtype or k_new.dtype != k_cache.dtype or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_new, v_new and the caches must share one dtype")
+    if k_new.shape != v_new.shape or k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k/v shapes or strides differ")
+    if k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new strides differ")
+    if cells.dtype != torch.int32 or cells.numel() != height * width:
+        raise ValueError("cells must be int32 [height*width]")
+    _contig(cells, "cells")
+    H, _, d = k_new.shape
+    kb_ptr, kb_ld = 0, 0
+    if kbar is not None:
+        if kbar.dtype != torch.float32:
+            raise ValueError("kbar must be float32")
+        kb_ptr, kb_ld = kbar.data_ptr(), _rows(kbar, "kbar")
+    lib = _lib.load()
+    _lib.check(lib.velox_kv_append(k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new),
+                                   _rows(k_new, "k_new"), H, T, height, width, d, chunk_index,
+                                   cells.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   _rows(k_cache, "k_cache"), token_offset, kb_ptr or None,
+                                   kb_ld, _stream(k_new)))

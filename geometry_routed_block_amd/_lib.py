@@ -1,5 +1,5 @@
-"""ctypes view of libvelox.so (the C ABI declared in include/velox.h and
-include/velox_geometry.h).
+"""ctypes view of libvelox.so (the C ABI declared in include/velox.h,
+include/velox_geometry.h and include/velox_layout.h).
 
 Loading fails loudly when the library has not been built: there is no
 fallback implementation.
@@ -20,7 +20,8 @@ VELOX_MAX_HISTORY = 16384
 
 EXPORTS = ("velox_last_error", "velox_version", "velox_block_mean", "velox_route_scores",
            "velox_route_select", "velox_sparse_attn", "velox_dense_attn",
-           "velox_slab_overlap", "velox_slab_coverage")
+           "velox_slab_overlap", "velox_slab_coverage", "velox_gilbert_curve",
+           "velox_kv_append")
 VELOX_OBB_WORDS = 16
 VELOX_MAX_LATTICE = 16
 
@@ -72,6 +73,11 @@ def load() -> ctypes.CDLL:
     lib.velox_slab_overlap.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.velox_slab_coverage.restype = i32
     lib.velox_slab_coverage.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.velox_gilbert_curve.restype = i32
+    lib.velox_gilbert_curve.argtypes = [i32, i32, vp]
+    lib.velox_kv_append.restype = i32
+    lib.velox_kv_append.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                    i64, i64, vp, i64, vp]
     lib.velox_dense_attn.restype = i32
     lib.velox_dense_attn.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
                                      vp, vp, vp]

@@ -28,6 +28,7 @@ UNITS = [
     ("velox_route.hip", ["-ffp-contract=off"]),
     ("velox_attn.hip", []),
     ("velox_geom.hip", ["-ffp-contract=off"]),
+    ("velox_layout.hip", []),
     ("velox_api.cpp", ["-x", "hip"]),
 ]
 

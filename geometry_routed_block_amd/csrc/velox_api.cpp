@@ -1,6 +1,7 @@
 // C ABI of libvelox: argument validation, error reporting and dispatch to the
 // kernel launchers. Declarations, layouts and the cited definitions of each
-// operation are in include/velox.h and include/velox_geometry.h.
+// operation are in include/velox.h, include/velox_geometry.h and
+// include/velox_layout.h.
 
 #include <hip/hip_runtime.h>
 
@@ -11,6 +12,7 @@
 
 #include "../../include/velox.h"
 #include "../../include/velox_geometry.h"
+#include "../../include/velox_layout.h"
 #include "velox_launch.hpp"
 
 namespace {
@@ -205,6 +207,49 @@ velox_status_t velox_slab_coverage(const float* q_pts, const float* h_obb, int N
   return launched(velox::launch_slab_coverage(q_pts, h_obb, N, M, token_mask, rho,
                                               static_cast<hipStream_t>(stream)),
                   "velox_slab_coverage");
+}
+
+velox_status_t velox_gilbert_curve(int width, int height, int32_t* cells) {
+  REQUIRE(width >= 1 && height >= 1, "width and height must be >= 1 (got %d x %d)", width, height);
+  REQUIRE(static_cast<int64_t>(width) * height <= VELOX_MAX_GRID_CELLS, "grid of %d x %d is too large",
+          width, height);
+  REQUIRE(cells, "cells must be non-NULL");
+  velox::gilbert_curve(width, height, cells);
+  return VELOX_OK;
+}
+
+velox_status_t velox_kv_append(const void* k_new, const void* v_new, velox_dtype_t dt,
+                               int64_t ld_new_h, int H, int T, int height, int width, int d,
+                               int chunk_index, const int32_t* cells, void* k_cache,
+                               void* v_cache, int64_t ld_kv_h, int64_t token_offset,
+                               float* kbar, int64_t ld_kbar_h, void* stream) {
+  REQUIRE(dtype_ok(dt), "dtype must be VELOX_F32 or VELOX_BF16");
+  REQUIRE(dim_ok(d), "d must be 64 or 128 (got %d)", d);
+  REQUIRE(H >= 1 && H <= 65535, "H must be in [1, 65535] (got %d)", H);
+  REQUIRE(T >= 1 && height >= 1 && width >= 1, "T, height and width must be >= 1");
+  REQUIRE(static_cast<int64_t>(height) * width <= VELOX_MAX_GRID_CELLS, "latent grid too large");
+  REQUIRE(chunk_index >= 0, "chunk_index must be >= 0");
+  const int64_t n_tok = static_cast<int64_t>(T) * height * width;
+  if (n_tok % VELOX_BLOCK != 0 || n_tok > (int64_t{1} << 30))
+    return fail(VELOX_ERR_UNSUPPORTED, "T*height*width=%lld is not a whole number of 128-token blocks",
+                static_cast<long long>(n_tok));
+  REQUIRE(token_offset >= 0 && token_offset % VELOX_BLOCK == 0, "token_offset must be a multiple of 128");
+  REQUIRE(k_new && v_new && cells && k_cache && v_cache, "k_new, v_new, cells and the caches must be non-NULL");
+  REQUIRE(ld_new_h >= n_tok * d, "ld_new_h too small");
+  REQUIRE(ld_kv_h >= (token_offset + n_tok) * d, "ld_kv_h too small for token_offset + chunk");
+  const int64_t nblk = n_tok / VELOX_BLOCK;
+  if (kbar) REQUIRE(ld_kbar_h >= (token_offset / VELOX_BLOCK + nblk) * d, "ld_kbar_h too small");
+  const int64_t eb = elem_bytes(dt);
+  REQUIRE(reinterpret_cast<uintptr_t>(k_new) % 16 == 0 && reinterpret_cast<uintptr_t>(v_new) % 16 == 0 &&
+              reinterpret_cast<uintptr_t>(k_cache) % 16 == 0 &&
+              reinterpret_cast<uintptr_t>(v_cache) % 16 == 0 && (ld_new_h * eb) % 16 == 0 &&
+              (ld_kv_h * eb) % 16 == 0,
+          "tensors and head strides must be 16-byte aligned");
+  return launched(velox::launch_kv_append(k_new, v_new, dt == VELOX_BF16, ld_new_h, H, T, height,
+                                          width, d, chunk_index, cells, k_cache, v_cache, ld_kv_h,
+                                          token_offset, kbar, ld_kbar_h,
+                                          static_cast<hipStream_t>(stream)),
+                  "velox_kv_append");
 }
 
 }  // extern "C"

@@ -45,6 +45,12 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
 hipError_t launch_attention(const AttnConfig& cfg, hipStream_t stream);
 hipError_t launch_slab_overlap(const float* q_obb, const float* h_obb, int N, int M, int n,
                                float* g, hipStream_t stream);
+void gilbert_curve(int width, int height, int32_t* cells);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, bool bf16, int64_t ld_new_h, int H,
+                            int T, int height, int width, int d, int chunk_index,
+                            const int32_t* cells, void* k_cache, void* v_cache, int64_t ld_kv_h,
+                            int64_t token_offset, float* kbar, int64_t ld_kbar_h,
+                            hipStream_t stream);
 hipError_t launch_slab_coverage(const float* q_pts, const float* h_obb, int N, int M,
                                 uint32_t* mask, float* rho, hipStream_t stream);
 

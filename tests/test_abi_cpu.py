@@ -129,3 +129,40 @@ def test_geometry_validation(lib):
     assert cv(None, BAD, 4, 16, BAD, BAD, None) == _lib.VELOX_ERR_INVALID
     assert cv(BAD, BAD, 4, -2, BAD, BAD, None) == _lib.VELOX_ERR_INVALID
     assert cv(None, None, 0, 5, None, None, None) == _lib.VELOX_OK
+
+
+def test_gilbert_curve_matches_the_oracle_on_the_host(lib):
+    # the curve is host code in the library: a full parity check without a GPU
+    import numpy as np
+    import geometry_routed_block_amd as velox
+    from oracle import layout
+    for w, h in [(1, 1), (2, 2), (9, 4), (4, 9), (52, 29), (29, 52), (48, 32), (16, 16), (13, 11),
+                 (1, 7), (7, 1), (3, 5), (64, 64), (100, 3)]:
+        got = velox.gilbert_curve(w, h)
+        ref = [y * w + x for x, y in layout.gilbert_curve(w, h)]
+        assert got.tolist() == ref, (w, h)
+
+
+def test_layout_validation(lib):
+    import numpy as np
+    cells = np.empty(4, np.int32)
+    assert lib.velox_gilbert_curve(0, 4, cells.ctypes.data) == _lib.VELOX_ERR_INVALID
+    assert lib.velox_gilbert_curve(1 << 13, 1 << 12, cells.ctypes.data) == _lib.VELOX_ERR_INVALID
+    assert lib.velox_gilbert_curve(2, 2, None) == _lib.VELOX_ERR_INVALID
+    f = lib.velox_kv_append
+    ld = 4608 * 128
+    args = dict(kn=BAD, vn=BAD, dt=1, ldn=ld, H=2, T=3, hh=32, ww=48, d=128, ci=0, cells=BAD,
+                kc=BAD, vc=BAD, ldkv=ld * 2, off=4608, kb=None, ldkb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["kn"], a["vn"], a["dt"], a["ldn"], a["H"], a["T"], a["hh"], a["ww"], a["d"], a["ci"],
+                 a["cells"], a["kc"], a["vc"], a["ldkv"], a["off"], a["kb"], a["ldkb"], None)
+    assert call(T=1, hh=29, ww=52) == _lib.VELOX_ERR_UNSUPPORTED      # 1508 tokens: not whole blocks
+    assert call(off=100) == _lib.VELOX_ERR_INVALID                     # unaligned offset
+    assert call(d=96) == _lib.VELOX_ERR_INVALID
+    assert call(ldkv=ld) == _lib.VELOX_ERR_INVALID                     # cache too small for offset + chunk
+    assert call(kb=BAD, ldkb=10) == _lib.VELOX_ERR_INVALID             # kbar stride too small
+    assert call(cells=None) == _lib.VELOX_ERR_INVALID
+    assert call(ci=-1) == _lib.VELOX_ERR_INVALID
+    assert call(kn=BAD + 8) == _lib.VELOX_ERR_INVALID                  # misaligned
