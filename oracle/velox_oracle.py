@@ -92,12 +92,31 @@ def ghat(g: np.ndarray, tau, g_ref) -> np.ndarray:
     return np.where(g > tau, ratio, np.float32(0.0)).astype(np.float32)
 
 
+def importance_shared(qbar_heads, kbar_heads, scale: float) -> np.ndarray:
+    """Head-shared importance [N][M]: softmax over r of the mean over heads of
+    scale * qbar_h . kbar_h (float64). The pages index p by layer only ([digest]
+    Method steps, step 4); this is its reading for a multi-head layer."""
+    qb = np.asarray(qbar_heads, dtype=np.float64)
+    kb = np.asarray(kbar_heads, dtype=np.float64)
+    logits = scale * np.einsum("hnd,hmd->nm", qb, kb) / qb.shape[0]
+    logits -= logits.max(axis=1, keepdims=True)
+    e = np.exp(logits)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+MODE_FUSED, MODE_MODEL_ONLY, MODE_GEOMETRY_ONLY = 0, 1, 2
+
+
 def fused_weights(p_row: np.ndarray, g_row: np.ndarray, rho_i, prm):
     """Unnormalised route weights w of one query block, in float32.
 
     Covered row (rho_i >= eta_cov): w = p * (1 + lambda * ghat), each product and
     sum rounded to float32. Uncovered row: w = p (the model's own distribution,
     untouched by geometry). Returns (w, covered).
+    Comparison routers ([project] 03 · Results: a matched model-only
+    block-sparse route; [digest] Prerequisites: soft fusion against hard
+    geometric top-K): mode 1 keeps w = p on covered rows too (same budgets),
+    mode 2 ranks covered rows by the overlap itself, w = g.
     Normalising w by its sum does not change the ranking, and the mass cut works
     on ratios, so the division of the formula is never materialised.
     """
@@ -105,6 +124,11 @@ def fused_weights(p_row: np.ndarray, g_row: np.ndarray, rho_i, prm):
     covered = bool(np.float32(rho_i) >= np.float32(prm.eta_cov))
     if not covered:
         return p_row.copy(), False
+    mode = int(getattr(prm, "mode", 0))
+    if mode == MODE_MODEL_ONLY:
+        return p_row.copy(), True
+    if mode == MODE_GEOMETRY_ONLY:
+        return np.asarray(g_row, dtype=np.float32).copy(), True
     gh = ghat(g_row, prm.tau, prm.g_ref)
     u = np.float32(1.0) + np.float32(prm.lam) * gh            # two float32 roundings
     return (p_row * u).astype(np.float32), True
@@ -140,6 +164,8 @@ def route_row(p_row, g_row, rho_i, prm, M: int, coords=None, query_block: int = 
     K = int(prm.K_cov if covered else prm.K_unc)
     theta = np.float32(prm.theta_cov if covered else prm.theta_unc)
     cut = bool(theta < np.float32(1.0))
+    if covered and int(getattr(prm, "mode", 0)) == MODE_GEOMETRY_ONLY:
+        cut = False            # overlaps are not a distribution: plain top-K_cov
     theta_q = int(Fraction(float(theta)) * (1 << THETA_BITS)) if cut else 0
     reserved_set = set(reserved)
     # Rank the other blocks by weight, heaviest first; equal weights by id.

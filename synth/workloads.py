@@ -45,6 +45,7 @@ class RouteParams:
     n_prev: int = 0             # last n_prev history ids are always kept
     neigh26: int = 0            # add Chebyshev-1 grid neighbours of the query block
     ref_ids: tuple = ()         # extra always-added history ids
+    mode: int = 0               # covered rows: 0 fused, 1 model only, 2 geometry only
 
     def replace(self, **kw) -> "RouteParams":
         return dataclasses.replace(self, **kw)
