@@ -240,6 +240,46 @@ def main():
         geo_ms[name] = round(gs.elapsed_time(ge) / 20, 4)
     log(f"geometry: overlap {geo_ms['slab_overlap']:.4f} ms, coverage {geo_ms['slab_coverage']:.4f} ms")
 
+    # comparison routers on the same tensors ([project] 03 · Results: matched
+    # model-only route; [digest]: hard geometric top-K; head-shared routes)
+    variants = {}
+    o_var = torch.empty_like(q)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name, mode in (("model_only", 1), ("geometry_only", 2)):
+        prm_v = wl.params.replace(mode=mode)
+        ids_v = torch.empty_like(ids)
+        lens_v = torch.empty_like(lens)
+
+        def run_v():
+            velox.route_select(p, g, rho, coord, prm_v, L=L, route_ids=ids_v, route_len=lens_v)
+            velox.sparse_attn(q, k, v, ids_v, lens_v, wl.M, out=o_var)
+        ms_v = timed(run_v)
+        variants[name] = {"select_plus_attn_ms": round(ms_v, 4),
+                          "tiles_visited": int((lens_v.cpu().numpy() + wl.N).sum())}
+    logits_ws = torch.empty(wl.H, wl.N, wl.M, device=dev)
+    p_sh = torch.empty(1, wl.N, wl.M, device=dev)
+    ids_sh = torch.empty(1, wl.N, L, dtype=torch.int32, device=dev)
+    lens_sh = torch.empty(1, wl.N, dtype=torch.int32, device=dev)
+
+    def run_shared():
+        velox.route_scores_shared(q, kbar, wl.M, logits=logits_ws, out=p_sh)
+        velox.route_select(p_sh, g, rho, coord, wl.params, L=L, route_ids=ids_sh, route_len=lens_sh)
+        velox.sparse_attn(q, k, v, ids_sh[0], lens_sh[0], wl.M, out=o_var)
+    variants["head_shared"] = {"step_ms": round(timed(run_shared), 4),
+                               "tiles_visited": int((lens_sh.cpu().numpy() + wl.N).sum()) * wl.H}
+    log(f"variants: {variants}")
+
     # KV append of one chunk in global order (once per chunk per layer, at
     # model QKV time: reported beside the step). 3 latent frames of 32 x 48
     # tokens = the 36 blocks of a chunk, written over the current chunk's rows
@@ -304,6 +344,7 @@ def main():
         "dense_ms": round(dense_ms, 4),
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
         "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
+        "router_variants": variants,
         "geometry_ms": geo_ms,
         "kv_append": {"ms": round(append_ms, 4), "bytes": append_bytes,
                       "gbps": round(append_bytes / append_ms / 1e6, 1),

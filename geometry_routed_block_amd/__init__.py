@@ -28,7 +28,7 @@ from ._lib import VELOX_BLOCK, VeloxError
 
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
            "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
-           "gilbert_curve", "kv_append", "library_path"]
+           "gilbert_curve", "kv_append", "route_scores_shared", "library_path"]
 
 
 def library_path() -> str:
@@ -107,6 +107,35 @@ def route_scores(q, kbar, M: int, scale: float | None = None, out=None):
     return out
 
 
+def route_scores_shared(q, kbar, M: int, scale: float | None = None, logits=None, out=None):
+    """Head-shared importance p [1][N][M] (softmax of the head-mean logits).
+
+    `logits` [H][N][M] fp32 is the per-head workspace (allocated if None).
+    """
+    torch = _torch()
+    _require_cuda(q, kbar)
+    H, NT, d = q.shape
+    N = NT // VELOX_BLOCK
+    if kbar.dtype != torch.float32:
+        raise TypeError("kbar must be float32")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if logits is None:
+        logits = torch.empty(H, N, M, dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty(1, N, M, dtype=torch.float32, device=q.device)
+    _require_cuda(logits, out)
+    _contig(logits, "logits")
+    _contig(out, "p")
+    if logits.numel() < H * N * M or out.numel() < N * M:
+        raise ValueError("logits must hold H*N*M and out N*M floats")
+    lib = _lib.load()
+    _lib.check(lib.velox_route_scores_shared(q.data_ptr(), _dtype_code(q), _rows(q, "q"),
+                                             kbar.data_ptr(), _rows(kbar, "kbar"), H, N, M, d,
+                                             ctypes.c_float(scale), logits.data_ptr(),
+                                             out.data_ptr(), _stream(q)))
+    return out
+
+
 def route_bound(params, M: int) -> int:
     """Smallest route length L that always suffices."""
     kmax = max(int(params.K_cov), int(params.K_unc), int(params.n_prev))
@@ -120,7 +149,8 @@ def route_select(p, g, rho, coord, params, L: int | None = None, route_ids=None,
 
     `params` is any object with the attributes tau, g_ref, lam, eta_cov,
     theta_cov, theta_unc, K_cov, K_unc, n_prev, neigh26 and ref_ids (a sequence
-    of history ids).
+    of history ids), and optionally mode (0 fused, 1 model only, 2 geometry
+    only; default 0).
     """
     torch = _torch()
     _require_cuda(p, g, rho)
@@ -144,7 +174,8 @@ def route_select(p, g, rho, coord, params, L: int | None = None, route_ids=None,
     c = _lib.RouteParamsC(params.tau, params.g_ref, params.lam, params.eta_cov, params.theta_cov,
                           params.theta_unc, int(params.K_cov), int(params.K_unc),
                           int(params.n_prev), int(params.neigh26),
-                          ref_t.data_ptr() if ref_t is not None else None, len(ref))
+                          ref_t.data_ptr() if ref_t is not None else None, len(ref),
+                          int(getattr(params, "mode", 0)))
     lib = _lib.load()
     _lib.check(lib.velox_route_select(p.data_ptr(), g.data_ptr(), rho.data_ptr(),
                                       coord.data_ptr() if coord is not None else None, H, N, M,
@@ -170,7 +201,11 @@ def _attn_out(q, out, lse, want_lse):
 
 def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = True,
                 scale: float | None = None, out=None, lse=None, want_lse: bool = False):
-    """Attention of each query block over its routed history tiles (+ current chunk)."""
+    """Attention of each query block over its routed history tiles (+ current chunk).
+
+    route_ids [H][N][L] / route_len [H][N] give one route per head; [N][L] / [N]
+    (or [1][N][L] / [1][N]) one route per query block shared by all heads.
+    """
     _require_cuda(q, k, v, route_ids, route_len)
     H, NT, d = q.shape
     N = NT // VELOX_BLOCK
@@ -181,12 +216,14 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
     lib = _lib.load()
-    _lib.check(lib.velox_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
-                                     _rows(q, "q"), _rows(k, "k"), H, N, M, d,
-                                     ctypes.c_float(scale), route_ids.data_ptr(),
-                                     route_len.data_ptr(), route_ids.shape[-1],
-                                     1 if include_current else 0, out.data_ptr(),
-                                     lse.data_ptr() if lse is not None else None, _stream(q)))
+    if route_len.numel() not in (N, H * N) or route_ids.numel() != route_len.numel() * route_ids.shape[-1]:
+        raise ValueError("routes must be [H][N][L] + [H][N] (per head) or [N][L] + [N] (shared)")
+    shared = route_len.numel() != H * N
+    fn = lib.velox_sparse_attn_shared if shared else lib.velox_sparse_attn
+    _lib.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), _rows(q, "q"),
+                  _rows(k, "k"), H, N, M, d, ctypes.c_float(scale), route_ids.data_ptr(),
+                  route_len.data_ptr(), route_ids.shape[-1], 1 if include_current else 0,
+                  out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q)))
     return (out, lse) if want_lse or lse is not None else out
 
 

@@ -21,7 +21,8 @@ VELOX_MAX_HISTORY = 16384
 EXPORTS = ("velox_last_error", "velox_version", "velox_block_mean", "velox_route_scores",
            "velox_route_select", "velox_sparse_attn", "velox_dense_attn",
            "velox_slab_overlap", "velox_slab_coverage", "velox_gilbert_curve",
-           "velox_kv_append")
+           "velox_kv_append", "velox_route_scores_shared", "velox_sparse_attn_shared")
+VELOX_ROUTE_FUSED, VELOX_ROUTE_MODEL_ONLY, VELOX_ROUTE_GEOMETRY_ONLY = 0, 1, 2
 VELOX_OBB_WORDS = 16
 VELOX_MAX_LATTICE = 16
 
@@ -33,6 +34,7 @@ class RouteParamsC(ctypes.Structure):
         ("eta_cov", ctypes.c_float), ("theta_cov", ctypes.c_float), ("theta_unc", ctypes.c_float),
         ("K_cov", ctypes.c_int32), ("K_unc", ctypes.c_int32), ("n_prev", ctypes.c_int32),
         ("neigh26", ctypes.c_int32), ("ref_ids", ctypes.c_void_p), ("n_ref", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
     ]
 
 
@@ -78,6 +80,11 @@ def load() -> ctypes.CDLL:
     lib.velox_kv_append.restype = i32
     lib.velox_kv_append.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                     i64, i64, vp, i64, vp]
+    lib.velox_route_scores_shared.restype = i32
+    lib.velox_route_scores_shared.argtypes = [vp, i32, i64, vp, i64, i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.velox_sparse_attn_shared.restype = i32
+    lib.velox_sparse_attn_shared.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
+                                             vp, vp, i32, i32, vp, vp, vp]
     lib.velox_dense_attn.restype = i32
     lib.velox_dense_attn.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
                                      vp, vp, vp]

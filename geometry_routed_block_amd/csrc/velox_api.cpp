@@ -126,6 +126,29 @@ velox_status_t velox_route_scores(const void* q, velox_dtype_t dt, int64_t ld_q_
                   "velox_route_scores");
 }
 
+velox_status_t velox_route_scores_shared(const void* q, velox_dtype_t dt, int64_t ld_q_h,
+                                         const float* kbar, int64_t ld_kbar_h, int H, int N, int M,
+                                         int d, float scale, float* logits, float* p,
+                                         void* stream) {
+  velox_status_t st = check_common(dt, H, N, M, d);
+  if (st != VELOX_OK) return st;
+  if (M == 0) return VELOX_OK;
+  REQUIRE(q && kbar && logits && p, "q, kbar, logits and p must be non-NULL");
+  REQUIRE(ld_q_h >= static_cast<int64_t>(N) * VELOX_BLOCK * d, "ld_q_h too small");
+  REQUIRE(ld_kbar_h >= static_cast<int64_t>(M) * d, "ld_kbar_h too small");
+  REQUIRE(std::isfinite(scale), "scale must be finite");
+  REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && (ld_q_h * elem_bytes(dt)) % 16 == 0,
+          "q and its head stride must be 16-byte aligned");
+  REQUIRE(reinterpret_cast<uintptr_t>(kbar) % 16 == 0 && ld_kbar_h % 4 == 0,
+          "kbar and its head stride must be 16-byte aligned");
+  if (velox::route_scores_lds_bytes(1, M, d) > velox::kMaxLdsBytes)
+    return fail(VELOX_ERR_UNSUPPORTED, "M=%d too large for route_scores", M);
+  return launched(velox::launch_route_scores_shared(q, dt == VELOX_BF16, ld_q_h, kbar, ld_kbar_h, H, N,
+                                                    M, d, scale, logits, p,
+                                                    static_cast<hipStream_t>(stream)),
+                  "velox_route_scores_shared");
+}
+
 velox_status_t velox_route_select(const float* p, const float* g, const float* rho,
                                   const int32_t* coord, int H, int N, int M,
                                   const velox_route_params_t* prm, int L, int32_t* route_ids,
@@ -146,32 +169,53 @@ velox_status_t velox_route_select(const float* p, const float* g, const float* r
   REQUIRE(prm->lambda >= 0.f && prm->lambda <= 14.f, "lambda must lie in [0, 14]");
   REQUIRE(prm->theta_cov > 0.f && prm->theta_unc > 0.f, "theta_cov and theta_unc must be > 0");
   REQUIRE(prm->neigh26 == 0 || prm->neigh26 == 1, "neigh26 must be 0 or 1");
+  REQUIRE(prm->mode >= VELOX_ROUTE_FUSED && prm->mode <= VELOX_ROUTE_GEOMETRY_ONLY,
+          "mode must be VELOX_ROUTE_FUSED, _MODEL_ONLY or _GEOMETRY_ONLY (got %d)", prm->mode);
   const long long kmax = prm->K_cov > prm->K_unc ? prm->K_cov : prm->K_unc;
   const long long base = kmax > prm->n_prev ? kmax : prm->n_prev;
   long long need = base + 26LL * prm->neigh26 + prm->n_ref;
   if (need > M) need = M;
   if (need < 1) need = 1;
   REQUIRE(L >= need, "L=%d is smaller than the route bound %lld", L, need);
-  velox::RouteConfig cfg{prm->tau,     prm->g_ref, prm->lambda, prm->eta_cov,
-                         prm->theta_cov, prm->theta_unc, prm->K_cov, prm->K_unc,
-                         prm->n_prev,  prm->neigh26, prm->ref_ids, prm->n_ref};
+  velox::RouteConfig cfg{prm->tau,       prm->g_ref,     prm->lambda, prm->eta_cov,
+                         prm->theta_cov, prm->theta_unc, prm->K_cov,  prm->K_unc,
+                         prm->n_prev,    prm->neigh26,   prm->mode,   prm->ref_ids,
+                         prm->n_ref};
   return launched(velox::launch_route_select(p, g, rho, coord, H, N, M, cfg, L, route_ids, route_len,
                                              static_cast<hipStream_t>(stream)),
                   "velox_route_select");
 }
 
-velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
-                                 int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
-                                 float scale, const int32_t* route_ids, const int32_t* route_len,
-                                 int L, int include_current, void* o, float* lse, void* stream) {
+static velox_status_t sparse_common(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                                    int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                                    float scale, const int32_t* route_ids, const int32_t* route_len,
+                                    int L, int include_current, void* o, float* lse, void* stream,
+                                    bool shared, const char* what) {
   velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
   if (st != VELOX_OK) return st;
   REQUIRE(route_ids && route_len, "route_ids and route_len must be non-NULL");
   REQUIRE(L >= 1, "L must be >= 1");
   REQUIRE(include_current == 0 || include_current == 1, "include_current must be 0 or 1");
   velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
-                      route_ids, route_len, L, include_current, o, lse};
-  return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), "velox_sparse_attn");
+                      route_ids, route_len, L, shared, include_current, o, lse};
+  return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), what);
+}
+
+velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                                 int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                                 float scale, const int32_t* route_ids, const int32_t* route_len,
+                                 int L, int include_current, void* o, float* lse, void* stream) {
+  return sparse_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, route_ids, route_len, L,
+                       include_current, o, lse, stream, false, "velox_sparse_attn");
+}
+
+velox_status_t velox_sparse_attn_shared(const void* q, const void* k, const void* v,
+                                        velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                        int N, int M, int d, float scale,
+                                        const int32_t* route_ids, const int32_t* route_len, int L,
+                                        int include_current, void* o, float* lse, void* stream) {
+  return sparse_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, route_ids, route_len, L,
+                       include_current, o, lse, stream, true, "velox_sparse_attn_shared");
 }
 
 velox_status_t velox_dense_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
@@ -180,7 +224,7 @@ velox_status_t velox_dense_attn(const void* q, const void* k, const void* v, vel
   velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
   if (st != VELOX_OK) return st;
   velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
-                      nullptr, nullptr, 0, 1, o, lse};
+                      nullptr, nullptr, 0, false, 1, o, lse};
   return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), "velox_dense_attn");
 }
 

@@ -54,10 +54,16 @@ struct AttnArgs {
   const int32_t* route_ids;
   const int32_t* route_len;
   int L;
+  int route_head_rows;  // route rows between heads: N (per-head routes) or 0 (shared)
   int include_current;
   void* o;
   float* lse;
 };
+
+// Route row of (head h, query block i).
+__device__ __forceinline__ int64_t route_row(const AttnArgs& a, int h, int i) {
+  return static_cast<int64_t>(h) * a.route_head_rows + i;
+}
 
 // Tile id of step j of a row. The current chunk's tiles come first (ncur of
 // them: N, or 0 without the current chunk): every query block of a head
@@ -245,8 +251,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int32_t* route = nullptr;
   int rlen = M;
   if (kRouted) {
-    route = a.route_ids + static_cast<int64_t>(row_id) * a.L;
-    rlen = min(max(a.route_len[row_id], 0), a.L);
+    const int64_t rr = route_row(a, h, i);
+    route = a.route_ids + rr * a.L;
+    rlen = min(max(a.route_len[rr], 0), a.L);
     if (M == 0) rlen = 0;
   }
   const int ncur = (!kRouted || a.include_current) ? a.N : 0;
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   for (int r = t; r < N; r += kThreads) {
     int rank = r;
     if (kRouted) {
-      const int* lens = a.route_len + static_cast<int64_t>(h) * N;
+      const int* lens = a.route_len + route_row(a, h, 0);
       const int lr = min(max(lens[r], 0), a.L);
       rank = 0;
       for (int o = 0; o < N; ++o) {
@@ -550,12 +557,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   int rlen = 0, ncur = 0;
   if (i >= 0) {
     rlen = M;
-    if (kRouted) rlen = M == 0 ? 0 : min(max(a.route_len[static_cast<int64_t>(h) * N + i], 0), a.L);
+    if (kRouted) rlen = M == 0 ? 0 : min(max(a.route_len[route_row(a, h, i)], 0), a.L);
     ncur = (!kRouted || a.include_current) ? N : 0;
   }
   const int S = 2 * (rlen + ncur);     // half-tiles of this team's row
   if (kRouted && i >= 0) {
-    const int32_t* route = a.route_ids + (static_cast<int64_t>(h) * N + i) * a.L;
+    const int32_t* route = a.route_ids + route_row(a, h, i) * a.L;
     for (int e = t - team * 256; e < rlen; e += 256) route_lds[team][e] = min(max(route[e], 0), M - 1);
   }
   if (tw == 0 && lane == 0) team_halves[team] = S;
@@ -776,8 +783,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int32_t* route = nullptr;
   int rlen = M;
   if (kRouted) {
-    route = a.route_ids + static_cast<int64_t>(row_id) * a.L;
-    rlen = min(max(a.route_len[row_id], 0), a.L);
+    const int64_t rr = route_row(a, h, i);
+    route = a.route_ids + rr * a.L;
+    rlen = min(max(a.route_len[rr], 0), a.L);
     if (M == 0) rlen = 0;
   }
   const int ncur = (!kRouted || a.include_current) ? a.N : 0;
@@ -864,6 +872,7 @@ hipError_t launch_attention(const AttnConfig& c, hipStream_t stream) {
   a.route_ids = c.route_ids;
   a.route_len = c.route_len;
   a.L = c.L;
+  a.route_head_rows = c.shared_routes ? 0 : c.N;
   a.include_current = c.include_current;
   a.o = c.o;
   a.lse = c.lse;

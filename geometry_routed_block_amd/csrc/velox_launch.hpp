@@ -11,7 +11,7 @@ constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
 
 struct RouteConfig {
   float tau, g_ref, lambda, eta_cov, theta_cov, theta_unc;
-  int K_cov, K_unc, n_prev, neigh26;
+  int K_cov, K_unc, n_prev, neigh26, mode;
   const int32_t* ref_ids;
   int n_ref;
 };
@@ -27,6 +27,7 @@ struct AttnConfig {
   const int32_t* route_ids;  // nullptr: dense (every history tile)
   const int32_t* route_len;
   int L;
+  bool shared_routes;        // one route per query block for every head
   int include_current;
   void* o;
   float* lse;
@@ -38,6 +39,9 @@ size_t route_scores_lds_bytes(int qb, int M, int d);
 hipError_t launch_route_scores(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
                                int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
                                float* p, hipStream_t stream);
+hipError_t launch_route_scores_shared(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
+                                      int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
+                                      float* logits, float* p, hipStream_t stream);
 size_t route_select_lds_bytes(int M);
 hipError_t launch_route_select(const float* p, const float* g, const float* rho,
                                const int32_t* coord, int H, int N, int M, const RouteConfig& cfg,

@@ -145,7 +145,8 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-template <typename T, int D, int QB>
+// kRaw: write the scaled logits (no softmax) to p, for the head-shared scores.
+template <typename T, int D, int QB, bool kRaw = false>
 __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     const T* __restrict__ q, int64_t ld_q_h, const float* __restrict__ kbar, int64_t ld_kbar_h,
     int N, int M, float scale, float* __restrict__ p) {
@@ -225,6 +226,14 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   }
   __syncthreads();
 
+  if (kRaw) {
+    for (int qb = 0; qb < nq; ++qb) {
+      float* out = p + (static_cast<int64_t>(h) * N + i0 + qb) * M;
+      for (int r = t; r < M; r += kScoreThreads) out[r] = logit[qb * M + r];
+    }
+    return;
+  }
+
   // 3. softmax over the history blocks of each row
   for (int qb = 0; qb < nq; ++qb) {
     float* lr = logit + qb * M;
@@ -241,6 +250,38 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     float* out = p + (static_cast<int64_t>(h) * N + i0 + qb) * M;
     for (int r = t; r < M; r += kScoreThreads) out[r] = lr[r] / sum;
   }
+}
+
+// ---------------------------------------------------------------- head-shared importance
+//
+// One workgroup per query block: the mean over heads (ascending h, then one
+// division by H) of the per-head scaled logits, then the softmax over the
+// history blocks, as in route_scores_kernel.
+__global__ __launch_bounds__(kScoreThreads) void head_mean_softmax_kernel(
+    const float* __restrict__ logits, int H, int N, int M, float* __restrict__ p) {
+  extern __shared__ float smem[];
+  float* red = smem;                 // [kScoreThreads / kWave]
+  float* lr = smem + kScoreThreads / kWave;
+  const int i = blockIdx.x, t = threadIdx.x;
+  const float fH = static_cast<float>(H);
+  for (int r = t; r < M; r += kScoreThreads) {
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) s += logits[(static_cast<int64_t>(h) * N + i) * M + r];
+    lr[r] = __fdiv_rn(s, fH);
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int r = t; r < M; r += kScoreThreads) mx = fmaxf(mx, lr[r]);
+  mx = block_max(mx, red);
+  float sum = 0.f;
+  for (int r = t; r < M; r += kScoreThreads) {
+    const float e = expf(lr[r] - mx);
+    lr[r] = e;
+    sum += e;
+  }
+  sum = block_sum(sum, red);
+  float* out = p + static_cast<int64_t>(i) * M;
+  for (int r = t; r < M; r += kScoreThreads) out[r] = lr[r] / sum;
 }
 
 // ---------------------------------------------------------------- route select
@@ -264,8 +305,13 @@ struct SelectArgs {
   int32_t* route_len;
   int N, M, L, P2, nwords;
   float tau, g_ref, lambda, eta_cov, theta_cov, theta_unc;
-  int K_cov, K_unc, n_prev, neigh26, n_ref;
+  int K_cov, K_unc, n_prev, neigh26, n_ref, mode;
 };
+
+// Route modes of a covered row (uncovered rows always use the model's p):
+//   0 fused:          w = p (1 + lambda ghat)          (the method)
+//   1 model only:     w = p                            (same budgets, no geometry)
+//   2 geometry only:  w = g, top-K_cov, no mass cut    (hard geometric top-K)
 
 constexpr int kSelectThreads = 512;
 
@@ -310,11 +356,13 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     uint64_t key = ~0ull;
     if (r < M) {
       float w = prow[r];
-      if (covered) {
+      if (covered && a.mode == 0) {
         const float g = grow[r];
         const float gh = (g > a.tau) ? fminf(__fdiv_rn(g, a.g_ref), 1.0f) : 0.0f;
         const float u = __fadd_rn(1.0f, __fmul_rn(a.lambda, gh));
         w = __fmul_rn(w, u);
+      } else if (covered && a.mode == 2) {
+        w = grow[r];
       }
       const uint64_t W = fixed_mass(w);
       zloc += W;
@@ -357,7 +405,8 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
 
   // 3. number of candidates taken after the reservation
   const int K = covered ? a.K_cov : a.K_unc;
-  const float theta = covered ? a.theta_cov : a.theta_unc;
+  // geometry-only rows take the plain top-K (overlaps are not a distribution)
+  const float theta = covered ? (a.mode == 2 ? 1.0f : a.theta_cov) : a.theta_unc;
   const int limit = max(0, min(K - n_res, M - n_res));
   int c = limit;
   if (theta < 1.0f && limit > 0) {
@@ -473,12 +522,12 @@ size_t route_scores_lds_bytes(int qb, int M, int d) {
                           static_cast<size_t>(qb) * M);
 }
 
-template <typename T, int D, int QB>
+template <typename T, int D, int QB, bool kRaw>
 static hipError_t scores_launch(const void* q, int64_t ld_q_h, const float* kbar,
                                 int64_t ld_kbar_h, int H, int N, int M, float scale, float* p,
                                 hipStream_t stream) {
   const size_t lds = route_scores_lds_bytes(QB, M, D);
-  auto kern = route_scores_kernel<T, D, QB>;
+  auto kern = route_scores_kernel<T, D, QB, kRaw>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
@@ -489,25 +538,50 @@ static hipError_t scores_launch(const void* q, int64_t ld_q_h, const float* kbar
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kRaw>
 static hipError_t scores_dispatch(const void* q, int64_t ld_q_h, const float* kbar,
                                   int64_t ld_kbar_h, int H, int N, int M, float scale, float* p,
                                   hipStream_t stream) {
   if (route_scores_lds_bytes(6, M, D) <= kMaxLdsBytes)
-    return scores_launch<T, D, 6>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+    return scores_launch<T, D, 6, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
   if (route_scores_lds_bytes(3, M, D) <= kMaxLdsBytes)
-    return scores_launch<T, D, 3>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
-  return scores_launch<T, D, 1>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+    return scores_launch<T, D, 3, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+  return scores_launch<T, D, 1, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+}
+
+template <bool kRaw>
+static hipError_t scores_any(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
+                             int64_t ld_kbar_h, int H, int N, int M, int d, float scale, float* p,
+                             hipStream_t stream) {
+  if (bf16)
+    return d == 128 ? scores_dispatch<bf16_t, 128, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream)
+                    : scores_dispatch<bf16_t, 64, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+  return d == 128 ? scores_dispatch<float, 128, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream)
+                  : scores_dispatch<float, 64, kRaw>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
 }
 
 hipError_t launch_route_scores(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
                                int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
                                float* p, hipStream_t stream) {
-  if (bf16)
-    return d == 128 ? scores_dispatch<bf16_t, 128>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream)
-                    : scores_dispatch<bf16_t, 64>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
-  return d == 128 ? scores_dispatch<float, 128>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream)
-                  : scores_dispatch<float, 64>(q, ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p, stream);
+  return scores_any<false>(q, bf16, ld_q_h, kbar, ld_kbar_h, H, N, M, d, scale, p, stream);
+}
+
+size_t head_mean_lds_bytes(int M) {
+  return sizeof(float) * (kScoreThreads / kWave + static_cast<size_t>(M));
+}
+
+hipError_t launch_route_scores_shared(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
+                                      int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
+                                      float* logits, float* p, hipStream_t stream) {
+  hipError_t e = scores_any<true>(q, bf16, ld_q_h, kbar, ld_kbar_h, H, N, M, d, scale, logits, stream);
+  if (e != hipSuccess) return e;
+  const size_t lds = head_mean_lds_bytes(M);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(head_mean_softmax_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_mean_softmax_kernel, dim3(N), dim3(kScoreThreads), lds, stream, logits, H,
+                     N, M, p);
+  return hipGetLastError();
 }
 
 size_t route_select_lds_bytes(int M) {
@@ -544,6 +618,7 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
   a.n_prev = cfg.n_prev;
   a.neigh26 = cfg.neigh26;
   a.n_ref = cfg.n_ref;
+  a.mode = cfg.mode;
   const size_t lds = route_select_lds_bytes(M);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -79,7 +79,16 @@ typedef struct {
                              budget); ids outside [0, M) are ignored; may be NULL
                              when n_ref == 0                                        */
   int32_t n_ref;
+  int32_t mode;     /* weights of a COVERED row (uncovered rows always use p):
+                       VELOX_ROUTE_FUSED (0, the method), VELOX_ROUTE_MODEL_ONLY
+                       (1, w = p with the same budgets: the matched model-only
+                       block-sparse route), VELOX_ROUTE_GEOMETRY_ONLY (2, w = g,
+                       plain top-K_cov with no mass cut: hard geometric top-K) */
 } velox_route_params_t;
+
+#define VELOX_ROUTE_FUSED 0
+#define VELOX_ROUTE_MODEL_ONLY 1
+#define VELOX_ROUTE_GEOMETRY_ONLY 2
 
 /* Message for the last non-OK status returned on this host thread. */
 const char* velox_last_error(void);
@@ -117,12 +126,33 @@ velox_status_t velox_route_scores(const void* q, velox_dtype_t dt, int64_t ld_q_
                                   int M, int d, float scale, float* p, void* stream);
 
 /*
+ * velox_route_scores_shared — one importance per layer instead of per head
+ * ([digest] Method steps, step 4 and [onedev] "What differs" index the
+ * importance p^l by layer only): p[i][r] = softmax over r of the mean over
+ * heads of scale * qbar_h . kbar_h (the head-mean of velox_route_scores'
+ * logits; ascending heads, then one division by H).
+ *   logits  [H][N][M] fp32 workspace, overwritten with the per-head scaled
+ *           logits (caller-owned)
+ *   p       [N][M] fp32 (output)
+ * Other arguments as velox_route_scores. Feed p to velox_route_select with
+ * H = 1 and the routes to velox_sparse_attn_shared.
+ */
+velox_status_t velox_route_scores_shared(const void* q, velox_dtype_t dt, int64_t ld_q_h,
+                                         const float* kbar, int64_t ld_kbar_h, int H, int N, int M,
+                                         int d, float scale, float* logits, float* p,
+                                         void* stream);
+
+/*
  * velox_route_select — route materialisation ([project] 02 · Method, fusion
  * formula and "Covered and uncovered blocks"; [digest] Core method and Method
  * steps, step 4, eq. 10-14; [onedev] "What differs").
  * Per (h, i), in IEEE fp32 without contraction:
  *   ghat = (g > tau) ? min(g / g_ref, 1) : 0
  *   w    = (rho[i] >= eta_cov) ? p * (1 + lambda * ghat) : p
+ * (covered rows under prm->mode = VELOX_ROUTE_MODEL_ONLY take w = p, under
+ * VELOX_ROUTE_GEOMETRY_ONLY w = g with no mass cut; [project] 03 · Results
+ * compares the method with a matched model-only block-sparse route, and
+ * [digest] Prerequisites contrasts soft fusion with hard geometric top-K)
  * Mass in fixed point: W = floor(w * 2^60), Z = sum_r W.
  * Route = reserved {M-n_prev .. M-1}, then the other blocks in order of w
  * (descending; equal w by ascending id) while |route| < K and, if theta < 1,
@@ -139,7 +169,8 @@ velox_status_t velox_route_scores(const void* q, velox_dtype_t dt, int64_t ld_q_
  *   route_len [H][N] int32 (output)
  * L must be >= min(M, max(K_cov, K_unc, n_prev) + 26*neigh26 + n_ref) and >= 1.
  * (With duplicated cells a row could exceed this; it is then cut to its L
- * smallest ids.) p rows must be non-negative with sum <= 1 + 2^-10.
+ * smallest ids.) p rows must be non-negative with sum <= 1 + 2^-10; g must be
+ * in [0, 1].
  */
 velox_status_t velox_route_select(const float* p, const float* g, const float* rho,
                                   const int32_t* coord, int H, int N, int M,
@@ -179,6 +210,18 @@ velox_status_t velox_dense_attn(const void* q, const void* k, const void* v,
                                 velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
                                 int N, int M, int d, float scale, void* o, float* lse,
                                 void* stream);
+
+/*
+ * velox_sparse_attn_shared — velox_sparse_attn with one route per query block
+ * shared by every head (routes of velox_route_scores_shared):
+ *   route_ids  [N][L] int32, route_len [N] int32
+ * Everything else as velox_sparse_attn.
+ */
+velox_status_t velox_sparse_attn_shared(const void* q, const void* k, const void* v,
+                                        velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                        int N, int M, int d, float scale,
+                                        const int32_t* route_ids, const int32_t* route_len, int L,
+                                        int include_current, void* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }
