@@ -1,0 +1,146 @@
+"""Pins of the slab-table and multiwarp oracle: numpy percentiles, hand-built
+blocks, closed-form boxes of a known camera, projection round trips and
+analytic planes seen from moved cameras. CPU only."""
+
+import numpy as np
+import pytest
+
+from oracle import slabs
+
+f32 = np.float32
+F, CX, CY = 26.0, 26.0, 14.5          # token-unit pinhole of a 52 x 29 grid
+
+
+def cam(R=np.eye(3), c=(0, 0, 0)):
+    out = np.zeros(12, f32)
+    out[0:9] = np.asarray(R, float).reshape(9)
+    out[9:12] = c
+    return out
+
+
+def rot(axis, ang):
+    a = np.asarray(axis, float) / np.linalg.norm(axis)
+    K = np.array([[0, -a[2], a[1]], [a[2], 0, -a[0]], [-a[1], a[0], 0]])
+    return np.eye(3) + np.sin(ang) * K + (1 - np.cos(ang)) * K @ K
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 10, 57, 128])
+def test_percentile_matches_numpy(n):
+    rng = np.random.default_rng(n)
+    x = np.sort(rng.lognormal(1.5, 0.5, n).astype(f32))
+    for p in (0.1, 0.5, 0.9):
+        ref = np.percentile(x.astype(np.float64), 100 * p)
+        assert abs(float(slabs.percentile(list(x), p)) - ref) <= 2e-6 * ref
+
+
+def test_slab_of_block_rectangle_interval_and_validity():
+    cols = np.array([3, 4, 5, 3, 9, 7] + [4] * 122)
+    rows = np.array([1, 1, 2, 3, 0, 2] + [2] * 122)
+    z = np.full(128, np.nan, f32)
+    z[:4] = [1.0, 2.0, 3.0, 4.0]
+    z[4] = 0.0          # unreliable: the column 9 / row 0 cell must not count
+    z[5] = -1.0         # unreliable
+    s = slabs.slab_of_block(cols, rows, z, n_min=4)
+    assert s.tolist()[:4] == [3, 6, 1, 4]
+    # float32 interpolation: within one float32 rounding of numpy's float64 value
+    assert abs(s[4] - 1.3) < 2e-6 * 1.3 and abs(s[5] - 3.7) < 2e-6 * 3.7
+    assert s[6] == 4 and s[7] == 1
+    assert slabs.slab_of_block(cols, rows, z, n_min=5)[7] == 0
+
+
+def test_box_of_a_centred_slab_at_identity_camera():
+    # a rectangle centred on the principal point, interval [2, 6]: the box sits
+    # on the optical axis at depth 4 with half-extents 4 w / (2 f), 4 h / (2 f), 2
+    slab = np.array([CX - 5, CX + 5, CY - 3, CY + 3, 2.0, 6.0, 100, 1], f32)
+    rec = slabs.slab_box(slab, cam(), F, CX, CY)
+    assert np.allclose(rec[0:3], [0, 0, 4], atol=1e-6)
+    assert np.allclose(rec[3:6], [4 * 10 / (2 * F), 4 * 6 / (2 * F), 2], rtol=1e-6)
+    assert (rec[6:15] == np.eye(3).reshape(9)).all()
+    assert (slabs.slab_box(np.zeros(8, f32), cam(), F, CX, CY) == 0).all()
+
+
+def test_box_face_corners_project_onto_the_rectangle():
+    R = rot([0.2, 1.0, -0.3], 0.8)
+    c = cam(R, (1.0, -2.0, 0.5))
+    slab = np.array([10, 17, 4, 9, 3.0, 5.0, 50, 1], f32)
+    rec = slabs.slab_box(slab, c, F, CX, CY)
+    centre, e, Rb = rec[0:3].astype(float), rec[3:6].astype(float), rec[6:15].astype(float).reshape(3, 3)
+    for sx, sy, u, v in ((-1, 1, 10, 4), (1, 1, 17, 4), (-1, -1, 10, 9), (1, -1, 17, 9)):
+        corner = centre + Rb @ np.array([sx * e[0], sy * e[1], 0.0])
+        pu, pv, pz = slabs.project(c, corner.astype(f32), F, CX, CY)
+        assert abs(pu - u) < 1e-4 and abs(pv - v) < 1e-4 and abs(pz - 4.0) < 1e-5
+
+
+def test_projection_round_trip():
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        c = cam(rot(rng.normal(size=3), rng.uniform(0, 3)), rng.normal(size=3))
+        u, v, z = rng.uniform(0, 52), rng.uniform(0, 29), rng.uniform(0.5, 20)
+        X = slabs.world_point(c, u, v, z, F, CX, CY)
+        pu, pv, pz = slabs.project(c, X, F, CX, CY)
+        assert abs(pu - u) < 1e-3 and abs(pv - v) < 1e-3 and abs(pz - z) < 1e-4 * z
+
+
+def _plane_depth(cam_rec, W, H, depth_along_axis):
+    """Depth map of a fronto-parallel plane (all pixels at the same depth)."""
+    return np.full(W * H, depth_along_axis, f32)
+
+
+def test_identity_warp_returns_the_depth_map():
+    W, H = 13, 7
+    rng = np.random.default_rng(2)
+    D = rng.uniform(1, 9, W * H).astype(f32)
+    D[5] = np.nan
+    c = cam(rot([1, 1, 0], 0.4), (0.3, 0.1, -2))
+    zq, chosen = slabs.multiwarp([D], [c], c, F / 4, W / 2, H / 2, W, H, k_warp=1)
+    ok = ~np.isnan(D)
+    assert np.allclose(zq[ok], D[ok], rtol=1e-5) and np.isnan(zq[5])
+    assert (chosen[ok] == 0).all() and chosen[5] == -1
+
+
+def test_newest_frame_with_enough_samples_wins():
+    # the target camera sits 2 units behind the source cameras (same axes), so
+    # several source pixels land in each target cell. Frame 0 sees a plane at
+    # depth 3, frame 1 (newer) one at depth 5 but only in the left half.
+    W, H, f = 16, 10, 8.0
+    src = cam(np.eye(3), (0, 0, 0))
+    tgt = cam(np.eye(3), (0, 0, -2.0))
+    D0 = _plane_depth(src, W, H, 3.0)
+    D1 = _plane_depth(src, W, H, 5.0)
+    D1.reshape(H, W)[:, W // 2:] = np.nan
+    zq, chosen = slabs.multiwarp([D0, D1], [src, src], tgt, f, W / 2, H / 2, W, H, k_warp=2)
+    zq, chosen = zq.reshape(H, W), chosen.reshape(H, W)
+    assert (chosen == 1).sum() > 0 and (chosen == 0).sum() > 0
+    assert np.allclose(zq[chosen == 1], 7.0, rtol=1e-5)     # 5 + 2 behind
+    assert np.allclose(zq[chosen == 0], 5.0, rtol=1e-5)     # 3 + 2 behind
+    # k_warp = 1 would take frame 1 wherever it lands at all
+    _, ch1 = slabs.multiwarp([D0, D1], [src, src], tgt, f, W / 2, H / 2, W, H, k_warp=1)
+    assert (ch1.reshape(H, W) == 1).sum() >= (chosen == 1).sum()
+
+
+def test_median_of_a_slanted_plane_matches_brute_force():
+    # a slanted plane seen by a source camera, warped into a rotated, shifted
+    # target: each cell's value is the median of the float64 re-projection of
+    # the newest frame's pixels that land in it
+    W, H, f = 12, 9, 7.0
+    src = cam(np.eye(3), (0, 0, 0))
+    tgt = cam(rot([0, 1, 0], 0.15), (0.4, 0.1, -1.5))
+    cols, rows = np.meshgrid(np.arange(W), np.arange(H))
+    D = (4.0 + 0.15 * cols + 0.1 * rows).astype(f32).ravel()
+    zq, chosen = slabs.multiwarp([D], [src], tgt, f, W / 2, H / 2, W, H, k_warp=2)
+    R = tgt[0:9].astype(float).reshape(3, 3)
+    t = tgt[9:12].astype(float)
+    lists = {}
+    for pix in range(W * H):
+        u, v = pix % W + 0.5, pix // W + 0.5
+        X = D[pix] * np.array([(u - W / 2) / f, (H / 2 - v) / f, 1.0])
+        p = R.T @ (X - t)
+        cu, cv = np.floor(f * p[0] / p[2] + W / 2), np.floor(H / 2 - f * p[1] / p[2])
+        if p[2] > 0 and 0 <= cu < W and 0 <= cv < H:
+            lists.setdefault(int(cv * W + cu), []).append(p[2])
+    checked = 0
+    for cidx, vals in lists.items():
+        if len(vals) >= 2 and chosen[cidx] == 0:
+            assert abs(zq[cidx] - np.median(vals)) < 1e-4
+            checked += 1
+    assert checked > 10
