@@ -238,7 +238,30 @@ def main():
         ge.record()
         torch.cuda.synchronize()
         geo_ms[name] = round(gs.elapsed_time(ge) / 20, 4)
-    log(f"geometry: overlap {geo_ms['slab_overlap']:.4f} ms, coverage {geo_ms['slab_coverage']:.4f} ms")
+    # slab table of one decoded chunk (36 blocks) and the multiwarp of the
+    # 60 cached first/last frames (4x token resolution) into chunk 48's camera
+    import synth.geometry as sgeo
+    hc, hd, hcam, hcob = sgeo.slab_inputs(n_chunks=1)
+    hc, hd, hcam, hcob = (torch.from_numpy(x).to(dev) for x in (hc, hd, hcam, hcob))
+    fr, fcams, fsize, fpin, tcam, tsize, tpin, qcells = sgeo.multiwarp_inputs()
+    fr, fcams, tcam, qcells = (torch.from_numpy(x).to(dev) for x in (fr, fcams, tcam, qcells))
+    ws = torch.empty(velox._lib.load().velox_multiwarp_workspace_size(fr.shape[0], *fsize, *tsize),
+                     dtype=torch.uint8, device=dev)
+    zq_b, _ = velox.multiwarp(fr, fcams, fsize, fpin, tcam, tsize, tpin, workspace=ws)
+    for name, fn in (("slab_table_36_blocks", lambda: velox.slab_table(hc, hd, hcam, hcob, *tpin)),
+                     ("multiwarp_60_frames", lambda: velox.multiwarp(fr, fcams, fsize, fpin, tcam, tsize, tpin,
+                                                                     workspace=ws)),
+                     ("token_points_4608", lambda: velox.token_points(qcells, zq_b, *tsize, tcam, *tpin))):
+        fn()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(20):
+            fn()
+        ge.record()
+        torch.cuda.synchronize()
+        geo_ms[name] = round(gs.elapsed_time(ge) / 20, 4)
+    log(f"geometry (ms): {geo_ms}")
 
     # comparison routers on the same tensors ([project] 03 · Results: matched
     # model-only route; [digest]: hard geometric top-K; head-shared routes)
@@ -349,7 +372,8 @@ def main():
         "kv_append": {"ms": round(append_ms, 4), "bytes": append_bytes,
                       "gbps": round(append_bytes / append_ms / 1e6, 1),
                       "frac_hbm": round(append_bytes / append_ms / 1e6 / PEAK_HBM_GBPS, 4)},
-        "geometry_point_tests": {"slab_overlap": wl.N * wl.M * 512, "slab_coverage": wl.N * 128 * wl.M},
+        "geometry_point_tests": {"slab_overlap": wl.N * wl.M * 512, "slab_coverage": wl.N * 128 * wl.M,
+                                 "multiwarp_samples": int(fr.numel())},
         "tiles_visited": tiles,
         "history_flop_share": round(flop_hist / flop, 4),
         "roofline": {

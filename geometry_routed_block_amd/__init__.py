@@ -2,7 +2,8 @@
 
 Thin PyTorch binding of libvelox.so: every function here only checks tensor
 metadata, marshals pointers and the current HIP stream, and calls the C ABI of
-include/velox.h, include/velox_geometry.h and include/velox_layout.h. All
+include/velox.h, include/velox_geometry.h, include/velox_layout.h and
+include/velox_slabs.h. All
 computation runs in the library's HIP kernels (the curve of velox_gilbert_curve
 is computed by the library's host code).
 
@@ -28,7 +29,8 @@ from ._lib import VELOX_BLOCK, VeloxError
 
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
            "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
-           "gilbert_curve", "kv_append", "route_scores_shared", "library_path"]
+           "gilbert_curve", "kv_append", "route_scores_shared", "slab_table", "multiwarp",
+           "token_points", "library_path"]
 
 
 def library_path() -> str:
@@ -331,3 +333,88 @@ def kv_append(k_new, v_new, T: int, height: int, width: int, chunk_index: int, c
                                    cells.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                    _rows(k_cache, "k_cache"), token_offset, kb_ptr or None,
                                    kb_ld, _stream(k_new)))
+
+
+def _f32c(t, name, shape_tail=None):
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if shape_tail is not None and tuple(t.shape[1:]) != tuple(shape_tail):
+        raise ValueError(f"{name} must be [n]{list(shape_tail)}")
+    _contig(t, name)
+
+
+def _i32c(t, name, shape_tail=None):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    if shape_tail is not None and tuple(t.shape[1:]) != tuple(shape_tail):
+        raise ValueError(f"{name} must be [n]{list(shape_tail)}")
+    _contig(t, name)
+
+
+def slab_table(cells, depth, cams, cam_of_block, f: float, cx: float, cy: float, n_min: int = 8):
+    """(slabs [nblk][8], boxes [nblk][16]) of blocks of 128 (cell, depth) samples."""
+    torch = _torch()
+    _require_cuda(cells, depth, cams, cam_of_block)
+    _i32c(cells, "cells", (2,))
+    _f32c(depth, "depth")
+    _f32c(cams, "cams", (12,))
+    _i32c(cam_of_block, "cam_of_block")
+    nblk = depth.numel() // VELOX_BLOCK
+    if depth.numel() != nblk * VELOX_BLOCK or cells.shape[0] != depth.numel() or cam_of_block.numel() != nblk:
+        raise ValueError("need 128 samples per block, one cell per sample, one camera per block")
+    slabs = torch.empty(nblk, 8, dtype=torch.float32, device=depth.device)
+    boxes = torch.empty(nblk, 16, dtype=torch.float32, device=depth.device)
+    lib = _lib.load()
+    _lib.check(lib.velox_slab_table(cells.data_ptr(), depth.data_ptr(), cams.data_ptr(),
+                                    cam_of_block.data_ptr(), cams.shape[0], nblk, f, cx, cy, n_min,
+                                    slabs.data_ptr(), boxes.data_ptr(), _stream(depth)))
+    return slabs, boxes
+
+
+def multiwarp(src_depth, src_cams, src_size, src_pinhole, tgt_cam, size, pinhole, k_warp: int = 2,
+              workspace=None):
+    """(zq [h*w] fp32, chosen [h*w] int32) by recency-priority multiwarp.
+
+    src_depth [K][src_h*src_w] depth frames with cameras src_cams [K][12],
+    src_size = (src_w, src_h), src_pinhole = (f, cx, cy) in pixels; the target
+    is a size = (w, h) token grid of tgt_cam [12] with pinhole (f, cx, cy).
+    """
+    torch = _torch()
+    _require_cuda(src_depth, src_cams, tgt_cam)
+    _f32c(src_depth, "src_depth")
+    _f32c(src_cams, "src_cams", (12,))
+    _f32c(tgt_cam, "tgt_cam")
+    K = src_cams.shape[0]
+    (sw, sh), (w, h) = src_size, size
+    if src_depth.numel() != K * sw * sh or tgt_cam.numel() != 12:
+        raise ValueError("src_depth must be [K][src_h*src_w] and tgt_cam [12]")
+    lib = _lib.load()
+    need = lib.velox_multiwarp_workspace_size(K, sw, sh, w, h)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=src_depth.device)
+    _require_cuda(workspace)
+    zq = torch.empty(w * h, dtype=torch.float32, device=src_depth.device)
+    chosen = torch.empty(w * h, dtype=torch.int32, device=src_depth.device)
+    _lib.check(lib.velox_multiwarp(src_depth.data_ptr(), src_cams.data_ptr(), K, sw, sh, *src_pinhole,
+                                   tgt_cam.data_ptr(), *pinhole, w, h, k_warp, zq.data_ptr(),
+                                   chosen.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream(src_depth)))
+    return zq, chosen
+
+
+def token_points(cells, zq, width: int, height: int, cam, f: float, cx: float, cy: float):
+    """(depth [n] fp32, points [n][3] fp32) of tokens from the warped depth map."""
+    torch = _torch()
+    _require_cuda(cells, zq, cam)
+    _i32c(cells, "cells", (2,))
+    _f32c(zq, "zq")
+    _f32c(cam, "cam")
+    n = cells.shape[0]
+    depth = torch.empty(n, dtype=torch.float32, device=cells.device)
+    pts = torch.empty(n, 3, dtype=torch.float32, device=cells.device)
+    lib = _lib.load()
+    _lib.check(lib.velox_token_points(cells.data_ptr(), zq.data_ptr(), width, height, cam.data_ptr(), f, cx,
+                                      cy, n, depth.data_ptr(), pts.data_ptr(), _stream(cells)))
+    return depth, pts

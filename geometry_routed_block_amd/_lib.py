@@ -1,5 +1,5 @@
 """ctypes view of libvelox.so (the C ABI declared in include/velox.h,
-include/velox_geometry.h and include/velox_layout.h).
+include/velox_geometry.h, include/velox_layout.h and include/velox_slabs.h).
 
 Loading fails loudly when the library has not been built: there is no
 fallback implementation.
@@ -21,7 +21,9 @@ VELOX_MAX_HISTORY = 16384
 EXPORTS = ("velox_last_error", "velox_version", "velox_block_mean", "velox_route_scores",
            "velox_route_select", "velox_sparse_attn", "velox_dense_attn",
            "velox_slab_overlap", "velox_slab_coverage", "velox_gilbert_curve",
-           "velox_kv_append", "velox_route_scores_shared", "velox_sparse_attn_shared")
+           "velox_kv_append", "velox_route_scores_shared", "velox_sparse_attn_shared",
+           "velox_slab_table", "velox_multiwarp_workspace_size", "velox_multiwarp",
+           "velox_token_points")
 VELOX_ROUTE_FUSED, VELOX_ROUTE_MODEL_ONLY, VELOX_ROUTE_GEOMETRY_ONLY = 0, 1, 2
 VELOX_OBB_WORDS = 16
 VELOX_MAX_LATTICE = 16
@@ -85,6 +87,15 @@ def load() -> ctypes.CDLL:
     lib.velox_sparse_attn_shared.restype = i32
     lib.velox_sparse_attn_shared.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
                                              vp, vp, i32, i32, vp, vp, vp]
+    lib.velox_slab_table.restype = i32
+    lib.velox_slab_table.argtypes = [vp, vp, vp, vp, i32, i32, f32, f32, f32, i32, vp, vp, vp]
+    lib.velox_multiwarp_workspace_size.restype = ctypes.c_size_t
+    lib.velox_multiwarp_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.velox_multiwarp.restype = i32
+    lib.velox_multiwarp.argtypes = [vp, vp, i32, i32, i32, f32, f32, f32, vp, f32, f32, f32, i32, i32,
+                                    i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.velox_token_points.restype = i32
+    lib.velox_token_points.argtypes = [vp, vp, i32, i32, vp, f32, f32, f32, i64, vp, vp, vp]
     lib.velox_dense_attn.restype = i32
     lib.velox_dense_attn.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
                                      vp, vp, vp]

@@ -29,6 +29,7 @@ UNITS = [
     ("velox_attn.hip", []),
     ("velox_geom.hip", ["-ffp-contract=off"]),
     ("velox_layout.hip", []),
+    ("velox_slabs.hip", ["-ffp-contract=off"]),
     ("velox_api.cpp", ["-x", "hip"]),
 ]
 

@@ -1,7 +1,7 @@
 // C ABI of libvelox: argument validation, error reporting and dispatch to the
 // kernel launchers. Declarations, layouts and the cited definitions of each
-// operation are in include/velox.h, include/velox_geometry.h and
-// include/velox_layout.h.
+// operation are in include/velox.h, include/velox_geometry.h,
+// include/velox_layout.h and include/velox_slabs.h.
 
 #include <hip/hip_runtime.h>
 
@@ -13,6 +13,7 @@
 #include "../../include/velox.h"
 #include "../../include/velox_geometry.h"
 #include "../../include/velox_layout.h"
+#include "../../include/velox_slabs.h"
 #include "velox_launch.hpp"
 
 namespace {
@@ -294,6 +295,75 @@ velox_status_t velox_kv_append(const void* k_new, const void* v_new, velox_dtype
                                           token_offset, kbar, ld_kbar_h,
                                           static_cast<hipStream_t>(stream)),
                   "velox_kv_append");
+}
+
+static velox_status_t check_pinhole(float f, float cx, float cy) {
+  REQUIRE(std::isfinite(f) && f > 0.f && std::isfinite(cx) && std::isfinite(cy),
+          "f must be finite and > 0, cx and cy finite");
+  return VELOX_OK;
+}
+
+velox_status_t velox_slab_table(const int32_t* cells, const float* depth, const float* cams,
+                                const int32_t* cam_of_block, int ncam, int nblk, float f,
+                                float cx, float cy, int n_min, float* slabs, float* boxes,
+                                void* stream) {
+  REQUIRE(nblk >= 0 && nblk <= (1 << 24), "nblk must lie in [0, 2^24] (got %d)", nblk);
+  if (nblk == 0) return VELOX_OK;
+  REQUIRE(ncam >= 1, "ncam must be >= 1");
+  REQUIRE(n_min >= 1 && n_min <= VELOX_BLOCK, "n_min must lie in [1, 128]");
+  velox_status_t st = check_pinhole(f, cx, cy);
+  if (st != VELOX_OK) return st;
+  REQUIRE(cells && depth && cams && cam_of_block && slabs && boxes, "pointers must be non-NULL");
+  return launched(velox::launch_slab_table(cells, depth, cams, cam_of_block, ncam, nblk, f, cx, cy, n_min,
+                                           slabs, boxes, static_cast<hipStream_t>(stream)),
+                  "velox_slab_table");
+}
+
+size_t velox_multiwarp_workspace_size(int K, int src_width, int src_height, int width, int height) {
+  if (K < 0 || src_width < 1 || src_height < 1 || width < 1 || height < 1) return 0;
+  return velox::multiwarp_workspace_bytes(K, src_width * src_height, width * height);
+}
+
+velox_status_t velox_multiwarp(const float* src_depth, const float* src_cams, int K, int src_width,
+                               int src_height, float src_f, float src_cx, float src_cy,
+                               const float* tgt_cam, float f, float cx, float cy, int width,
+                               int height, int k_warp, float* zq, int32_t* chosen,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(K >= 0 && K <= 4096, "K must lie in [0, 4096] (got %d)", K);
+  REQUIRE(width >= 1 && height >= 1 && static_cast<int64_t>(width) * height <= (1 << 22),
+          "target grid must be at least 1 x 1 and at most 2^22 cells");
+  REQUIRE(src_width >= 1 && src_height >= 1 && static_cast<int64_t>(src_width) * src_height <= (1 << 24),
+          "source frames must be at least 1 x 1 and at most 2^24 pixels");
+  REQUIRE(static_cast<int64_t>(K) * src_width * src_height <= (int64_t{1} << 30), "K * pixels too large");
+  REQUIRE(k_warp >= 1, "k_warp must be >= 1");
+  velox_status_t st = check_pinhole(f, cx, cy);
+  if (st != VELOX_OK) return st;
+  st = check_pinhole(src_f, src_cx, src_cy);
+  if (st != VELOX_OK) return st;
+  REQUIRE(tgt_cam && zq && chosen && workspace, "tgt_cam, zq, chosen and workspace must be non-NULL");
+  REQUIRE(K == 0 || (src_depth && src_cams), "src_depth and src_cams must be non-NULL when K > 0");
+  REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 4 == 0, "workspace must be 4-byte aligned");
+  const size_t need = velox::multiwarp_workspace_bytes(K, src_width * src_height, width * height);
+  REQUIRE(workspace_bytes >= need, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+          need);
+  return launched(velox::launch_multiwarp(src_depth, src_cams, K, src_width, src_height, src_f, src_cx, src_cy,
+                                          tgt_cam, f, cx, cy, width, height, k_warp, zq, chosen, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                  "velox_multiwarp");
+}
+
+velox_status_t velox_token_points(const int32_t* cells, const float* zq, int width, int height,
+                                  const float* cam, float f, float cx, float cy, int64_t n_tok,
+                                  float* depth, float* pts, void* stream) {
+  REQUIRE(n_tok >= 0 && n_tok <= (int64_t{1} << 30), "n_tok out of range");
+  if (n_tok == 0) return VELOX_OK;
+  REQUIRE(width >= 1 && height >= 1, "grid must be at least 1 x 1");
+  velox_status_t st = check_pinhole(f, cx, cy);
+  if (st != VELOX_OK) return st;
+  REQUIRE(cells && zq && cam && depth && pts, "pointers must be non-NULL");
+  return launched(velox::launch_token_points(cells, zq, width, height, cam, f, cx, cy, n_tok, depth, pts,
+                                             static_cast<hipStream_t>(stream)),
+                  "velox_token_points");
 }
 
 }  // extern "C"

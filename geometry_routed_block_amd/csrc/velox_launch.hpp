@@ -50,6 +50,17 @@ hipError_t launch_attention(const AttnConfig& cfg, hipStream_t stream);
 hipError_t launch_slab_overlap(const float* q_obb, const float* h_obb, int N, int M, int n,
                                float* g, hipStream_t stream);
 void gilbert_curve(int width, int height, int32_t* cells);
+hipError_t launch_slab_table(const int32_t* cells, const float* depth, const float* cams,
+                             const int32_t* cam_of_block, int ncam, int nblk, float f, float cx, float cy,
+                             int n_min, float* slabs, float* boxes, hipStream_t stream);
+size_t multiwarp_workspace_bytes(int K, int P, int C);
+hipError_t launch_multiwarp(const float* src_depth, const float* src_cams, int K, int SW, int SH, float fs,
+                            float cxs, float cys, const float* tgt_cam, float ft, float cxt, float cyt, int W,
+                            int H, int k_warp, float* zq, int32_t* chosen, void* workspace,
+                            hipStream_t stream);
+hipError_t launch_token_points(const int32_t* cells, const float* zq, int W, int H, const float* cam,
+                               float f, float cx, float cy, int64_t n_tok, float* depth, float* pts,
+                               hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, bool bf16, int64_t ld_new_h, int H,
                             int T, int height, int width, int d, int chunk_index,
                             const int32_t* cells, void* k_cache, void* v_cache, int64_t ld_kv_h,

@@ -36,9 +36,10 @@ Readings where the pages are silent (listed in the design notes):
   centre at the interval's mid-depth, axes = the camera axes, lateral
   half-extents = the rectangle's half-size at mid-depth, depth half-extent =
   half the interval;
-- multiwarp: a source pixel lands in target cell (floor(u'), floor(v')) when
-  its point is in front of the target camera and inside the grid; frames are
-  ranked by their index (higher = newer).
+- multiwarp: the cached frames are depth maps at their own (pixel) resolution
+  and pinhole; a source pixel lands in target token cell (floor(u'), floor(v'))
+  when its point is in front of the target camera and inside the grid; frames
+  are ranked by their index (higher = newer).
 
 Precision: every decision (reliable or not, which cell a warped point lands in)
 and every output is computed in IEEE float32, one rounding per operation, in the
@@ -163,24 +164,29 @@ def slab_table(cells, depth, cams, cam_of_block, f, cx, cy, n_min):
     return slabs, boxes
 
 
-def multiwarp(src_depth, src_cams, tgt_cam, f, cx, cy, width, height, k_warp=2):
+def multiwarp(src_depth, src_cams, src_w, src_h, src_pin, tgt_cam, width, height, tgt_pin,
+              k_warp=2):
     """(zq [height*width] float32, NaN = none; chosen frame [height*width] int, -1 = none).
 
-    src_depth [K][height*width] float32 depth maps on the same token grid as
-    the target, frame k newer than frame k-1; src_cams [K][12].
+    src_depth [K][src_h*src_w] float32 depth maps (row-major pixels) of frames
+    with cameras src_cams [K][12] and pinhole src_pin = (f, cx, cy); frame k is
+    newer than frame k-1. The target is a width x height token grid seen by
+    tgt_cam with pinhole tgt_pin.
     """
     K = len(src_depth)
     C = width * height
+    fs, cxs, cys = src_pin
+    ft, cxt, cyt = tgt_pin
     samples = [[[] for _ in range(K)] for _ in range(C)]
     for k in range(K):
-        for pix in range(C):
+        for pix in range(src_w * src_h):
             z = src_depth[k][pix]
             if not reliable(z):
                 continue
-            col, row = pix % width, pix // width
-            X = world_point(src_cams[k], f32(col) + f32(0.5), f32(row) + f32(0.5), z, f, cx, cy)
-            u, v, dz = project(tgt_cam, X, f, cx, cy)
-            if not (dz > 0):
+            col, row = pix % src_w, pix // src_w
+            X = world_point(src_cams[k], f32(col) + f32(0.5), f32(row) + f32(0.5), z, fs, cxs, cys)
+            u, v, dz = project(tgt_cam, X, ft, cxt, cyt)
+            if not (dz > 0) or not (np.isfinite(u) and np.isfinite(v)):
                 continue
             fu, fv = math.floor(float(u)), math.floor(float(v))
             if 0 <= fu < width and 0 <= fv < height:
@@ -196,3 +202,21 @@ def multiwarp(src_depth, src_cams, tgt_cam, f, cx, cy, width, height, k_warp=2):
                 chosen[c] = k
                 break
     return zq, chosen
+
+
+def token_points(cells, zq, width, height, cam, f, cx, cy):
+    """(depth [n] float32, points [n][3] float32) of tokens at cells [n][2]:
+    the warped depth of the token's cell and its world point (NaN without
+    depth)."""
+    cells = np.asarray(cells)
+    n = cells.shape[0]
+    depth = np.empty(n, f32)
+    pts = np.full((n, 3), np.nan, f32)
+    for s_ in range(n):
+        col = min(max(int(cells[s_, 0]), 0), width - 1)
+        row = min(max(int(cells[s_, 1]), 0), height - 1)
+        z = f32(zq[row * width + col])
+        depth[s_] = z
+        if reliable(z):
+            pts[s_] = world_point(cam, f32(col) + f32(0.5), f32(row) + f32(0.5), z, f, cx, cy)
+    return depth, pts

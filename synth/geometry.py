@@ -167,3 +167,104 @@ def assign_coverage(n_query: int, covered_fraction: float,
     rho = rng.uniform(0.0, 0.85, size=n_query)
     rho[perm[:n_cov]] = rng.uniform(0.9, 1.0, size=n_cov)
     return rho.astype(np.float32)
+
+
+# ---------------------------------------------------------------- depth scene
+#
+# Inputs of the slab-table and multiwarp kernels: depth maps of an analytic
+# scene (the inside of a sphere of radius 8 around the origin, which the
+# looping camera never leaves) rendered from the trajectory's cameras, and the
+# token cells plus depths of history blocks. The rendering is closed-form
+# ray-sphere intersection, which is not part of the method.
+
+ROOM_RADIUS = 8.0
+
+
+def pack_camera(rot: np.ndarray, centre: np.ndarray) -> np.ndarray:
+    """float32 [12]: R row-major (columns = camera axes in world), then centre."""
+    out = np.zeros(12, np.float32)
+    out[0:9] = np.asarray(rot, np.float64).reshape(9)
+    out[9:12] = centre
+    return out
+
+
+def sphere_room_depth(rot, centre, width, height, pinhole, rng=None, invalid_fraction=0.0):
+    """float32 [height*width] camera-z depth of the room wall through each pixel
+    centre (col + 0.5, row + 0.5); a random `invalid_fraction` of pixels is NaN."""
+    f, cx, cy = pinhole
+    cols, rows = np.meshgrid(np.arange(width) + 0.5, np.arange(height) + 0.5)
+    rays = np.stack([(cols - cx) / f, (cy - rows) / f, np.ones_like(cols)], -1).reshape(-1, 3)
+    w = rays @ np.asarray(rot, np.float64).T                 # world directions (z-component 1 in camera)
+    c = np.asarray(centre, np.float64)
+    a = (w * w).sum(1)
+    b = 2 * (w @ c)
+    cc = c @ c - ROOM_RADIUS ** 2
+    t = (-b + np.sqrt(b * b - 4 * a * cc)) / (2 * a)           # the far root: camera is inside
+    depth = t.astype(np.float32)
+    if rng is not None and invalid_fraction > 0:
+        depth[rng.uniform(size=depth.size) < invalid_fraction] = np.nan
+    return depth
+
+
+def slab_inputs(seed: int = 7, n_chunks: int = 6, blocks_per_chunk: int = 36):
+    """History blocks of n_chunks chunks: cells [nblk*128][2] int32, depth
+    [nblk*128] float32 (10% unreliable), cams [n_chunks][12], cam_of_block."""
+    rng = np.random.default_rng(seed)
+    pin = (FOCAL, TOKEN_W / 2, TOKEN_H / 2)
+    cams = np.stack([pack_camera(*camera_pose(c)) for c in range(n_chunks)])
+    nblk = n_chunks * blocks_per_chunk
+    cells = np.zeros((nblk * 128, 2), np.int32)
+    depth = np.zeros(nblk * 128, np.float32)
+    cam_of_block = np.repeat(np.arange(n_chunks), blocks_per_chunk).astype(np.int32)
+    for b in range(nblk):
+        c0, r0 = rng.integers(0, TOKEN_W - 8), rng.integers(0, TOKEN_H - 6)
+        cw, rh = rng.integers(2, 9), rng.integers(2, 7)
+        col = rng.integers(c0, c0 + cw, 128)
+        row = rng.integers(r0, r0 + rh, 128)
+        cells[128 * b:128 * b + 128] = np.stack([col, row], 1)
+        rot, ctr = camera_pose(int(cam_of_block[b]))
+        full = sphere_room_depth(rot, ctr, TOKEN_W, TOKEN_H, pin)
+        z = full[row * TOKEN_W + col] * rng.lognormal(0.0, 0.05, 128).astype(np.float32)
+        z[rng.uniform(size=128) < 0.1] = np.nan
+        depth[128 * b:128 * b + 128] = z
+    if nblk > 3:   # a few degenerate blocks: all unreliable, or barely any depth
+        depth[128 * 1:128 * 2] = np.nan
+        depth[128 * 2:128 * 3 - 3] = -1.0
+    return cells, depth, cams, cam_of_block
+
+
+def multiwarp_inputs(target_chunk: int = 48, n_cached: int = 30, scale: int = 4, seed: int = 11,
+                     holes: bool = True):
+    """Cached first/last-frame depth of the n_cached chunks before target_chunk
+    at `scale` x the token resolution, their cameras, the target camera, the
+    pinholes, and the token cells of the target chunk's 36 blocks. With
+    `holes`, the newest chunk's frames lack depth in their left third and the
+    one before in its top quarter (unreconstructed regions), so older frames
+    must fill in."""
+    rng = np.random.default_rng(seed)
+    sw, sh = TOKEN_W * scale, TOKEN_H * scale
+    src_pin = (FOCAL * scale, sw / 2, sh / 2)
+    tgt_pin = (FOCAL, TOKEN_W / 2, TOKEN_H / 2)
+    frames, cams = [], []
+    for c in range(target_chunk - n_cached, target_chunk):
+        for frac in (0.0, 0.9):            # first and last frame of the chunk
+            rot, ctr = camera_pose(c + frac)
+            frames.append(sphere_room_depth(rot, ctr, sw, sh, src_pin, rng, invalid_fraction=0.05))
+            cams.append(pack_camera(rot, ctr))
+    if holes and len(frames) >= 4:
+        for k in (-1, -2):
+            frames[k].reshape(sh, sw)[:, : sw // 3] = np.nan
+        for k in (-3, -4):
+            frames[k].reshape(sh, sw)[: sh // 4] = np.nan
+    tgt = pack_camera(*camera_pose(target_chunk))
+    # tokens of the 36 blocks on the 4 x 9 block grid: a block covers its
+    # rectangle of cells (3 frames), padded to 128 by repeating its cells
+    rects = block_rectangles(4, 9)
+    cells = np.zeros((36 * 128, 2), np.int32)
+    for b in range(36):
+        u0, u1, v0, v1 = rects[b // 9, b % 9]
+        cc = [(c, r) for r in range(int(np.floor(v0)), int(np.ceil(v1))) for c in range(int(np.floor(u0)),
+                                                                                     int(np.ceil(u1)))]
+        tok = (cc * ((128 // len(cc)) + 1))[:128]
+        cells[128 * b:128 * b + 128] = tok
+    return (np.stack(frames), np.stack(cams), (sw, sh), src_pin, tgt, (TOKEN_W, TOKEN_H), tgt_pin, cells)

@@ -166,3 +166,25 @@ def test_layout_validation(lib):
     assert call(cells=None) == _lib.VELOX_ERR_INVALID
     assert call(ci=-1) == _lib.VELOX_ERR_INVALID
     assert call(kn=BAD + 8) == _lib.VELOX_ERR_INVALID                  # misaligned
+
+
+def test_slabs_validation(lib):
+    st = lib.velox_slab_table
+    assert st(BAD, BAD, BAD, BAD, 1, 4, 26.0, 26.0, 14.5, 0, BAD, BAD, None) == _lib.VELOX_ERR_INVALID   # n_min 0
+    assert st(BAD, BAD, BAD, BAD, 0, 4, 26.0, 26.0, 14.5, 8, BAD, BAD, None) == _lib.VELOX_ERR_INVALID   # ncam 0
+    assert st(BAD, BAD, BAD, BAD, 1, 4, -1.0, 26.0, 14.5, 8, BAD, BAD, None) == _lib.VELOX_ERR_INVALID  # f <= 0
+    assert st(None, None, None, None, 1, 0, 26.0, 26.0, 14.5, 8, None, None, None) == _lib.VELOX_OK      # nblk 0
+    assert lib.velox_multiwarp_workspace_size(60, 208, 116, 52, 29) >= 60 * 208 * 116 * 12
+    mw = lib.velox_multiwarp
+    need = lib.velox_multiwarp_workspace_size(2, 16, 8, 8, 4)
+
+    def call(k_warp=2, nbytes=need, ws=BAD, src=BAD, sf=8.0):
+        return mw(src, BAD, 2, 16, 8, sf, 8.0, 4.0, BAD, 4.0, 4.0, 2.0, 8, 4, k_warp, BAD, BAD, ws, nbytes, None)
+    assert call(k_warp=0) == _lib.VELOX_ERR_INVALID
+    assert call(nbytes=need - 4) == _lib.VELOX_ERR_INVALID
+    assert call(ws=BAD + 2) == _lib.VELOX_ERR_INVALID
+    assert call(src=None) == _lib.VELOX_ERR_INVALID
+    assert call(sf=0.0) == _lib.VELOX_ERR_INVALID
+    tp = lib.velox_token_points
+    assert tp(None, None, 8, 4, None, 4.0, 4.0, 2.0, 0, None, None, None) == _lib.VELOX_OK
+    assert tp(BAD, BAD, 0, 4, BAD, 4.0, 4.0, 2.0, 10, BAD, BAD, None) == _lib.VELOX_ERR_INVALID

@@ -92,7 +92,8 @@ def test_identity_warp_returns_the_depth_map():
     D = rng.uniform(1, 9, W * H).astype(f32)
     D[5] = np.nan
     c = cam(rot([1, 1, 0], 0.4), (0.3, 0.1, -2))
-    zq, chosen = slabs.multiwarp([D], [c], c, F / 4, W / 2, H / 2, W, H, k_warp=1)
+    pin = (F / 4, W / 2, H / 2)
+    zq, chosen = slabs.multiwarp([D], [c], W, H, pin, c, W, H, pin, k_warp=1)
     ok = ~np.isnan(D)
     assert np.allclose(zq[ok], D[ok], rtol=1e-5) and np.isnan(zq[5])
     assert (chosen[ok] == 0).all() and chosen[5] == -1
@@ -108,13 +109,14 @@ def test_newest_frame_with_enough_samples_wins():
     D0 = _plane_depth(src, W, H, 3.0)
     D1 = _plane_depth(src, W, H, 5.0)
     D1.reshape(H, W)[:, W // 2:] = np.nan
-    zq, chosen = slabs.multiwarp([D0, D1], [src, src], tgt, f, W / 2, H / 2, W, H, k_warp=2)
+    pin = (f, W / 2, H / 2)
+    zq, chosen = slabs.multiwarp([D0, D1], [src, src], W, H, pin, tgt, W, H, pin, k_warp=2)
     zq, chosen = zq.reshape(H, W), chosen.reshape(H, W)
     assert (chosen == 1).sum() > 0 and (chosen == 0).sum() > 0
     assert np.allclose(zq[chosen == 1], 7.0, rtol=1e-5)     # 5 + 2 behind
     assert np.allclose(zq[chosen == 0], 5.0, rtol=1e-5)     # 3 + 2 behind
     # k_warp = 1 would take frame 1 wherever it lands at all
-    _, ch1 = slabs.multiwarp([D0, D1], [src, src], tgt, f, W / 2, H / 2, W, H, k_warp=1)
+    _, ch1 = slabs.multiwarp([D0, D1], [src, src], W, H, pin, tgt, W, H, pin, k_warp=1)
     assert (ch1.reshape(H, W) == 1).sum() >= (chosen == 1).sum()
 
 
@@ -127,7 +129,8 @@ def test_median_of_a_slanted_plane_matches_brute_force():
     tgt = cam(rot([0, 1, 0], 0.15), (0.4, 0.1, -1.5))
     cols, rows = np.meshgrid(np.arange(W), np.arange(H))
     D = (4.0 + 0.15 * cols + 0.1 * rows).astype(f32).ravel()
-    zq, chosen = slabs.multiwarp([D], [src], tgt, f, W / 2, H / 2, W, H, k_warp=2)
+    pin = (f, W / 2, H / 2)
+    zq, chosen = slabs.multiwarp([D], [src], W, H, pin, tgt, W, H, pin, k_warp=2)
     R = tgt[0:9].astype(float).reshape(3, 3)
     t = tgt[9:12].astype(float)
     lists = {}
@@ -144,3 +147,17 @@ def test_median_of_a_slanted_plane_matches_brute_force():
             assert abs(zq[cidx] - np.median(vals)) < 1e-4
             checked += 1
     assert checked > 10
+
+
+def test_higher_resolution_source_fills_every_cell():
+    # a source frame at 4x the token resolution, seen from the same camera:
+    # every target cell receives 16 samples of the same plane depth
+    W, H, f = 10, 6, 5.0
+    c = cam(rot([0, 0, 1], 0.3), (0.1, 0.2, 0.3))
+    D = np.full(4 * W * 4 * H, 6.0, f32)
+    zq, chosen = slabs.multiwarp([D], [c], 4 * W, 4 * H, (4 * f, 2 * W, 2 * H), c, W, H, (f, W / 2, H / 2),
+                                 k_warp=16)
+    assert (chosen == 0).all() and np.allclose(zq, 6.0, rtol=1e-5)
+    zq2, chosen2 = slabs.multiwarp([D], [c], 4 * W, 4 * H, (4 * f, 2 * W, 2 * H), c, W, H, (f, W / 2, H / 2),
+                                   k_warp=17)
+    assert (chosen2 == -1).all() and np.isnan(zq2).all()
