@@ -13,8 +13,6 @@ What the pages fix, and what this generator takes from them:
   Prerequisites, "frustum slab and OBB overlap": a historical KV block is
   summarised by its token rectangle and a percentile depth interval, approximated
   by a camera-facing OBB; two blocks correspond by intersection-volume ratio.
-- Same digest, Method steps, step 1: the depth interval is the 10/90
-  percentile of the block's depths.
 - Velox project page, 02 · Method, "What the router sees": top overlaps of a
   query block with its best history blocks are around 0.4-0.7 (a magnitude
   check for this generator, not a value it must reproduce).
@@ -67,12 +65,15 @@ def _token_depths(rng: np.random.Generator, n: int) -> np.ndarray:
 
 def slab_obbs(coords: np.ndarray, chunk_of_block: np.ndarray, blocks_h: int,
               blocks_w: int, rng: np.random.Generator, depths: np.ndarray | None = None):
-    """Camera-facing OBBs (centre [n,3], axes [n,3,3], half-extents [n,3]).
+    """Scene boxes (centre [n,3], axes [n,3,3], half-extents [n,3]) of the blocks.
 
-    Per block: depth samples ~ lognormal(mu=1.5, sigma=0.5) (or `depths`),
-    interval [Q10, Q90]; the box sits on the ray through the rectangle centre at
-    the interval's mid-depth, its axes are the camera axes, its lateral extents
-    are the rectangle's extents at mid-depth and its depth extent the interval.
+    Per block, token depths ~ lognormal(mu=1.5, sigma=0.5) (or `depths`); the
+    box sits on the ray through the block rectangle's centre at the mean depth,
+    its axes are the camera axes, its lateral half-extents are the rectangle's
+    half-size at the mean depth and its depth half-extent is 1.28 standard
+    deviations of the depths (a normal spread's 10-90 half-width). A
+    generator's moment recipe; the method's own slabs come from percentile
+    intervals and are built by the slab-table kernel.
     """
     rects = block_rectangles(blocks_h, blocks_w)
     n = coords.shape[0]
@@ -84,15 +85,13 @@ def slab_obbs(coords: np.ndarray, chunk_of_block: np.ndarray, blocks_h: int,
     for b in range(n):
         _, bh, bw = coords[b]
         rot, cam = camera_pose(int(chunk_of_block[b]))
-        zlo, zhi = np.quantile(depths[b], [0.10, 0.90])
-        zmid = 0.5 * (zlo + zhi)
+        zm, zs = float(np.mean(depths[b])), float(np.std(depths[b]))
         u0, u1, v0, v1 = rects[bh, bw]
         uc, vc = 0.5 * (u0 + u1), 0.5 * (v0 + v1)
         ray = np.array([(uc - TOKEN_W / 2) / FOCAL, (TOKEN_H / 2 - vc) / FOCAL, 1.0])
-        centre[b] = cam + rot @ (zmid * ray)
+        centre[b] = cam + rot @ (zm * ray)
         axes[b] = rot
-        half[b] = (zmid * (u1 - u0) / (2 * FOCAL), zmid * (v1 - v0) / (2 * FOCAL),
-                   0.5 * (zhi - zlo))
+        half[b] = (zm * (u1 - u0) / (2 * FOCAL), zm * (v1 - v0) / (2 * FOCAL), 1.2816 * zs)
     return centre, axes, half
 
 
