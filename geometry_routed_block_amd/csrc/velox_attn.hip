@@ -495,17 +495,28 @@ __device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
   return reinterpret_cast<const bf16_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// The four instructions are written in inline assembly so that the compiler
+// does not see an LDS DMA in flight: when it does, it treats LDS reads as
+// completing out of order and waits for every outstanding LDS read before each
+// MFMA, which serialises the fragment loads of the MFMA phases. The kernel
+// orders the DMA itself (explicit vmcnt waits, then a workgroup barrier, before
+// any wave reads a slot), and no code in it uses M0 otherwise. s_nop 4 covers
+// the M0 write and a scalar base freshly computed from a VALU result.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_half(lds_char_t* slot, const bf16_t* src_any, uint32_t lane_off, int tw) {
   gbl_char_t* sb = (gbl_char_t*)uniform_ptr(src_any);
+  const uint32_t l0 =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot))) + tw * 1024;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // opaque 32-bit offset per load: keeps the scalar-base + 32-bit-offset
-    // addressing form (no 64-bit address arithmetic per load)
-    uint32_t off = lane_off + i * 4096;
-    asm volatile("" : "+v"(off));
-    __builtin_amdgcn_global_load_lds(sb + off, slot + (tw + 4 * i) * 1024, 16, 0, 0);
+    const uint32_t off = lane_off + i * 4096;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(l0 + i * 4096), "v"(off), "s"(sb)
+                 : "memory", "m0");
   }
 }
+#pragma clang diagnostic pop
 
 template <bool kRouted>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
@@ -529,25 +540,83 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int N = a.N, M = a.M;
   const int pairs = (N + 1) / 2;
   const int G = (a.G / N) * pairs;
-  const int wg = xcd_remap(blockIdx.x, G);
-  const int h = wg / pairs, pr = wg % pairs;
-
-  // ---- this workgroup's two query blocks: rows of head h ranked by route
-  // length (longest first, ties by index); the pair is ranks 2 pr and 2 pr + 1.
+  // ---- which (head, pair) this workgroup serves. A pair is two rows of one
+  // head, ranks 2 pr and 2 pr + 1 of its rows ordered by route length (longest
+  // first, ties by index). Each XCD owns a contiguous range of (head, pair) ids
+  // (xcd_remap). Routed: the XCD's workgroups, in dispatch order, take that
+  // range's pairs longest first (longest-processing-time order, so that the
+  // short pairs fill the tail of the grid); the order is computed here from the
+  // route lengths, staged in route_lds before the route ids use it.
+  int* lens_s = &route_lds[0][0];
+  int h, pr;
   if (t < 2) pair_rows[t] = -1;
-  __syncthreads();
-  for (int r = t; r < N; r += kThreads) {
-    int rank = r;
-    if (kRouted) {
-      const int* lens = a.route_len + route_row(a, h, 0);
-      const int lr = min(max(lens[r], 0), a.L);
-      rank = 0;
-      for (int o = 0; o < N; ++o) {
-        const int lo = min(max(lens[o], 0), a.L);
-        rank += (lo > lr) || (lo == lr && o < r);
+  if (kRouted) {
+    const int x = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+    int base, cnt;
+    xcd_range(x, G, base, cnt);
+    const int h_lo = base / pairs, nh = (base + cnt - 1) / pairs - h_lo + 1;
+    const int nr = nh * N;
+    int* rank_s = lens_s + nr;
+    int* cost_s = rank_s + nr;
+    int* sorted_s = cost_s + cnt;
+    if (4 * nr <= 2 * kMaxRoute && cnt <= nr) {
+      for (int e = t; e < nr; e += kThreads)
+        lens_s[e] = min(max(a.route_len[route_row(a, h_lo + e / N, e % N)], 0), a.L);
+      __syncthreads();
+      for (int e = t; e < nr; e += kThreads) {
+        const int hb = e - e % N, lr = lens_s[e];
+        int rank = 0;
+        for (int o = hb; o < hb + N; ++o) rank += (lens_s[o] > lr) || (lens_s[o] == lr && o < e);
+        rank_s[e] = rank;
+        sorted_s[hb + rank] = lr;
+      }
+      __syncthreads();
+      for (int w = t; w < cnt; w += kThreads) {
+        const int id = base + w;
+        cost_s[w] = sorted_s[(id / pairs - h_lo) * N + 2 * (id % pairs)];
+      }
+      __syncthreads();
+      for (int w = t; w < cnt; w += kThreads) {
+        const int cw = cost_s[w];
+        int rank = 0;
+        for (int v = 0; v < cnt; ++v) rank += (cost_s[v] > cw) || (cost_s[v] == cw && v < w);
+        if (rank == slot) pair_rows[0] = base + w;  // the one pair of dispatch rank `slot`
+      }
+      __syncthreads();
+      const int wg = pair_rows[0];
+      h = wg / pairs;
+      pr = wg % pairs;
+      __syncthreads();
+      if (t < 2) pair_rows[t] = -1;
+      __syncthreads();
+      for (int r = t; r < N; r += kThreads) {
+        const int rank = rank_s[(h - h_lo) * N + r];
+        if (rank / 2 == pr) pair_rows[rank & 1] = r;
+      }
+    } else {
+      // too many rows to stage: dispatch order of the logical ids
+      const int wg = xcd_remap(blockIdx.x, G);
+      h = wg / pairs;
+      pr = wg % pairs;
+      __syncthreads();
+      for (int r = t; r < N; r += kThreads) {
+        const int* lens = a.route_len + route_row(a, h, 0);
+        const int lr = min(max(lens[r], 0), a.L);
+        int rank = 0;
+        for (int o = 0; o < N; ++o) {
+          const int lo = min(max(lens[o], 0), a.L);
+          rank += (lo > lr) || (lo == lr && o < r);
+        }
+        if (rank / 2 == pr) pair_rows[rank & 1] = r;
       }
     }
-    if (rank / 2 == pr) pair_rows[rank & 1] = r;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, G);
+    h = wg / pairs;
+    pr = wg % pairs;
+    __syncthreads();
+    for (int r = t; r < N; r += kThreads)
+      if (r / 2 == pr) pair_rows[r & 1] = r;
   }
   __syncthreads();
   const int i = pair_rows[team];  // -1: this team has no block (odd N)
@@ -621,36 +690,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     tile = __builtin_amdgcn_readfirstlane(tile);
     return base + (static_cast<int64_t>(tile) * kBlock + (j & 1) * kHalf) * D;
   };
+  // fragment loads: V^T (ks, db) of the PV product, K (kb, ds) of the QK one
+  auto load_v = [&](lds_char_t* vs, int ks, int db) {
+    lds_char_t* vp = vs + v_off[db] + ks * 16 * 256;
+    const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp));
+    const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 8 * 256));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto load_k = [&](lds_char_t* ksl, int kb, int ds) {
+    return __builtin_bit_cast(bf16x8_t, *(const lds_u32x4_t*)(ksl + kb * 8192 + ((ds << 5) ^ kz1)));
+  };
+  // Each MFMA phase is two streams of 16 MFMAs (PV(j-1), then K(j) Q^T with
+  // the two key blocks alternating, so consecutive MFMAs never depend on each
+  // other); every fragment is loaded from LDS kAhead MFMAs before its use.
+  // Scheduling fences keep that order: left alone, the compiler waits for
+  // each load right after issuing it.
+  constexpr int kAhead = 3;
+  auto pv_stream = [&](lds_char_t* vs) {
+    bf16x8_t fb[16];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) fb[u] = load_v(vs, u >> 2, u & 3);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + kAhead < 16) fb[u + kAhead] = load_v(vs, (u + kAhead) >> 2, (u + kAhead) & 3);
+      o_acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u], pf[u >> 2], o_acc[u & 3], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto qk_stream = [&](lds_char_t* ksl) {
+    bf16x8_t fb[16];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) fb[u] = load_k(ksl, u & 1, u >> 1);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + kAhead < 16) fb[u + kAhead] = load_k(ksl, (u + kAhead) & 1, (u + kAhead) >> 1);
+      const int kb = u & 1, ds = u >> 1;
+      s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u], qf[ds], ds == 0 ? f32x16_t{} : s_acc[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   // P: parity of j (Even / Odd), Q: the other parity
   auto mfma_phase = [&](int j, auto P, auto Q) {
-    if (j > 0) {  // O += P(j-1) V(j-1)
-      lds_char_t* vs = vslot(Q);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          lds_char_t* vp = vs + v_off[db] + ks * 16 * 256;
-          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp));
-          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 8 * 256));
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o_acc[db], 0, 0, 0);
-        }
-      }
-    }
-    if (j < S) {  // S(j) = K(j) Q^T
-      lds_char_t* ksl = kslot(P) + kbase;
-      const int z1 = kz1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s_acc[kb] = f32x16_t{};
-#pragma unroll
-        for (int ds = 0; ds < 8; ++ds) {
-          const bf16x8_t kf =
-              __builtin_bit_cast(bf16x8_t, *(const lds_u32x4_t*)(ksl + kb * 8192 + ((ds << 5) ^ z1)));
-          s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s_acc[kb], 0, 0, 0);
-        }
-      }
-    }
+    if (j > 0) pv_stream(vslot(Q));             // O += P(j-1) V(j-1)
+    if (j < S) qk_stream(kslot(P) + kbase);     // S(j) = K(j) Q^T
+  };
+  // a workgroup barrier that no instruction is scheduled across
+  auto phase_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_nofence();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   auto valu_phase = [&](int j, auto P, auto Q) {
@@ -666,7 +756,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       m1 = fmaxf(m1, s_acc[1][r]);
     }
     float mx = fmaxf(m0, m1);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+    {  // lanes l and l ^ 32 hold the same query: exchange halves without LDS
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
+    }
     if (__ballot(mx > m_ref + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -702,6 +795,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       tracked_wait_vm_all();
   };
 
+  // The output pointers are not needed before the end, but a scalar load
+  // still in flight makes every LDS wait in the loop a wait for all LDS
+  // reads (scalar loads return out of order): have them in registers now.
+  asm volatile("" ::"s"(a.o), "s"(a.lse));
   // prologue: K(0), K(1), V(0)
   if (S > 0) {
     dma_half(kslot(Even{}), half_src(kh, 0), koff_dma, tw);
@@ -718,9 +815,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   }
   auto step = [&](int j, auto P, auto Q) {
     mfma_phase(j, P, Q);
-    barrier_nofence();
+    phase_barrier();
     if (j < S) valu_phase(j, P, Q);
-    barrier_nofence();
+    phase_barrier();
   };
   if (S > 0) {
     for (int j = 0; j <= S; j += 2) {  // S is even

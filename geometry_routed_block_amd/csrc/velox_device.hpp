@@ -32,11 +32,17 @@ template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) {
 // Workgroup ids are dispatched round-robin over the 8 XCDs of an MI355X.
 // Remap so that consecutive logical ids land on the same XCD (and share its
 // L2): XCD x receives a contiguous range of logical ids. Bijective on [0, G).
+constexpr int kXcd = 8;
 __device__ __forceinline__ int xcd_remap(int b, int G) {
-  constexpr int kXcd = 8;
   const int per = G / kXcd, rem = G % kXcd;
   const int x = b % kXcd, slot = b / kXcd;
   return x < rem ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+}
+// The contiguous logical range [base, base + cnt) that xcd_remap gives XCD x.
+__device__ __forceinline__ void xcd_range(int x, int G, int& base, int& cnt) {
+  const int per = G / kXcd, rem = G % kXcd;
+  base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  cnt = per + (x < rem ? 1 : 0);
 }
 
 }  // namespace velox
