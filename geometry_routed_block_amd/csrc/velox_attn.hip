@@ -500,21 +500,23 @@ __device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
 // completing out of order and waits for every outstanding LDS read before each
 // MFMA, which serialises the fragment loads of the MFMA phases. The kernel
 // orders the DMA itself (explicit vmcnt waits, then a workgroup barrier, before
-// any wave reads a slot), and no code in it uses M0 otherwise. s_nop 4 covers
-// the M0 write and a scalar base freshly computed from a VALU result.
+// any wave reads a slot), and no code in it uses M0 otherwise. The leading
+// s_nop 4 covers a scalar base freshly computed from a VALU result, each
+// s_nop 0 the M0 write before the load that reads it.
+// src: wave-uniform global address of the half-tile; m0s[i]: LDS address of
+// instruction i (slot + (tw + 4 i) KiB); off[i]: this lane's byte offset.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_half(lds_char_t* slot, const bf16_t* src_any, uint32_t lane_off, int tw) {
-  gbl_char_t* sb = (gbl_char_t*)uniform_ptr(src_any);
-  const uint32_t l0 =
-      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot))) + tw * 1024;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t off = lane_off + i * 4096;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
-                 ::"s"(l0 + i * 4096), "v"(off), "s"(sb)
-                 : "memory", "m0");
-  }
+__device__ __forceinline__ void dma_half(gbl_char_t* src, const uint32_t (&m0s)[4], const uint32_t (&off)[4]) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %8\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %8\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %8\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %8"
+      ::"s"(m0s[0]), "s"(m0s[1]), "s"(m0s[2]), "s"(m0s[3]),
+        "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(src)
+      : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -649,6 +651,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   auto vslot = [&](auto P) {
     return (lds_char_t*)(decltype(P)::value ? v_odd : v_even) + team * kSlot;
   };
+  auto kslot_any = [&](int par) { return (lds_char_t*)(par ? k_odd : k_even) + team * kSlot; };
+  auto vslot_any = [&](int par) { return (lds_char_t*)(par ? v_odd : v_even) + team * kSlot; };
   using Even = std::integral_constant<int, 0>;
   using Odd = std::integral_constant<int, 1>;
   const uint32_t koff_dma = dma_lane_off(tw, lane, false);
@@ -684,12 +688,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     v_off[db] = r * 256 + ((c ^ ((r << 2) & 15)) << 4) + (gi & 1) * 8;
   }
 
-  auto half_src = [&](const bf16_t* base, int j) {
-    const int jt = j >> 1;
-    int tile = jt < ncur ? M + jt : (kRouted ? route_lds[team][jt - ncur] : jt - ncur);
-    tile = __builtin_amdgcn_readfirstlane(tile);
-    return base + (static_cast<int64_t>(tile) * kBlock + (j & 1) * kHalf) * D;
+  // Byte offset of half-tile j within the head's K or V. The route id of a
+  // half-tile is read from LDS one phase ahead, during the MFMA phase, where
+  // its latency hides behind the MFMA stream (route_raw; for every j, clamped
+  // inside route_lds, so no branch surrounds the read); half_off selects and
+  // scales. j may pass the end of the row by two: the result is then unused.
+  auto route_raw = [&](int j) {
+    const int e = min(max((j >> 1) - ncur, 0), kMaxRoute - 1);
+    return kRouted ? route_lds[team][e] : 0;
   };
+  auto half_off = [&](int j, int id) -> uint64_t {
+    const int jt = j >> 1;
+    const int tile = jt < ncur ? M + jt : (kRouted ? id : jt - ncur);
+    return static_cast<uint64_t>(static_cast<uint32_t>(tile)) * (kBlock * D * 2) + (j & 1) * (kHalf * D * 2);
+  };
+  gbl_char_t* const kg = (gbl_char_t*)uniform_ptr(kh);
+  gbl_char_t* const vg = (gbl_char_t*)uniform_ptr(vh);
+  uint32_t koff[4], voff[4], m0k[2][4], m0v[2][4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    koff[n] = koff_dma + n * 4096;
+    voff[n] = voff_dma + n * 4096;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      m0k[par][n] = __builtin_amdgcn_readfirstlane(
+          static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kslot_any(par))) + (tw + 4 * n) * 1024);
+      m0v[par][n] = __builtin_amdgcn_readfirstlane(
+          static_cast<uint32_t>(reinterpret_cast<uintptr_t>(vslot_any(par))) + (tw + 4 * n) * 1024);
+    }
+  }
+  uint64_t hoff_next = 0;  // byte offset of half-tile j + 1 (K(j+1), then V(j+1))
+  int id_next = 0;         // route id of half-tile j + 2
   // fragment loads: V^T (ks, db) of the PV product, K (kb, ds) of the QK one
   auto load_v = [&](lds_char_t* vs, int ks, int db) {
     lds_char_t* vp = vs + v_off[db] + ks * 16 * 256;
@@ -733,8 +762,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   };
   // P: parity of j (Even / Odd), Q: the other parity
   auto mfma_phase = [&](int j, auto P, auto Q) {
+    const int rid = route_raw(j + 2);
     if (j > 0) pv_stream(vslot(Q));             // O += P(j-1) V(j-1)
     if (j < S) qk_stream(kslot(P) + kbase);     // S(j) = K(j) Q^T
+    id_next = __builtin_amdgcn_readfirstlane(rid);
   };
   // a workgroup barrier that no instruction is scheduled across
   auto phase_barrier = [] {
@@ -746,8 +777,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   auto valu_phase = [&](int j, auto P, auto Q) {
     // refill the slots MFMA(j) just freed: K(j+2) into K(j)'s, V(j+1) into V(j-1)'s
     const bool k_next = j + 2 < S, v_next = j + 1 < S;
-    if (k_next) dma_half(kslot(P), half_src(kh, j + 2), koff_dma, tw);
-    if (v_next) dma_half(vslot(Q), half_src(vh, j + 1), voff_dma, tw);
+    const uint64_t hk = half_off(j + 2, id_next);
+    if (k_next) dma_half(kg + hk, m0k[decltype(P)::value], koff);
+    if (v_next) dma_half(vg + hoff_next, m0v[decltype(Q)::value], voff);
+    hoff_next = hk;
     // softmax of S(j) against the lazy reference max
     float m0 = s_acc[0][0], m1 = s_acc[1][0];
 #pragma unroll
@@ -800,10 +833,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // reads (scalar loads return out of order): have them in registers now.
   asm volatile("" ::"s"(a.o), "s"(a.lse));
   // prologue: K(0), K(1), V(0)
-  if (S > 0) {
-    dma_half(kslot(Even{}), half_src(kh, 0), koff_dma, tw);
-    dma_half(vslot(Even{}), half_src(vh, 0), voff_dma, tw);
-    if (S > 1) dma_half(kslot(Odd{}), half_src(kh, 1), koff_dma, tw);
+  if (S > 0) {  // S >= 2
+    const uint64_t h0 = half_off(0, __builtin_amdgcn_readfirstlane(route_raw(0)));
+    dma_half(kg + h0, m0k[0], koff);
+    dma_half(vg + h0, m0v[0], voff);
+    hoff_next = half_off(1, __builtin_amdgcn_readfirstlane(route_raw(1)));
+    dma_half(kg + hoff_next, m0k[1], koff);
   }
   tracked_wait_vm_all();
   barrier_nofence();
