@@ -288,11 +288,16 @@ __global__ __launch_bounds__(kScoreThreads) void head_mean_softmax_kernel(
 //
 // One workgroup (512 threads) per (query block, head).
 //  1. fused weight w (fp32, one rounding per operation), fixed-point mass W,
-//     total Z and reserved mass; sort key = (~bits(w) << 32) | id so that an
-//     ascending sort ranks by w descending, then id ascending (w >= 0).
-//  2. bitonic sort of the keys in LDS.
+//     total Z and reserved mass; sort key = (~bits(w) << 32) | id so that
+//     ascending key order ranks by w descending, then id ascending (w >= 0);
+//     the keys are distinct.
+//  2. the `limit` smallest keys (limit = the cap): a radix select, 8 bits at a
+//     time from the top, finds the bucket of the limit-th smallest key, the
+//     keys up to it are gathered and, when a mass cut follows, put in order by
+//     counting for each the keys below it. (A cap above kFastSel falls back to
+//     a bitonic sort of all keys.)
 //  3. count c of taken candidates: the cap, or the first prefix whose mass
-//     meets the threshold (block-wide scan of the sorted masses).
+//     meets the threshold (block-wide scan of the ordered masses).
 //  4. route = reserved ∪ first c ∪ safeguards as an LDS bitmask; emit ascending.
 
 struct SelectArgs {
@@ -314,6 +319,13 @@ struct SelectArgs {
 //   2 geometry only:  w = g, top-K_cov, no mass cut    (hard geometric top-K)
 
 constexpr int kSelectThreads = 512;
+constexpr int kFastSel = 1024;   // largest cap served by the radix select
+
+// Control words of the radix select, in LDS.
+struct SelectCtl {
+  uint64_t prefix;
+  int rank, cnt, n;
+};
 
 __device__ __forceinline__ uint64_t fixed_mass(float w) {
   // w * 2^60 is exact in double (24-bit significand, power-of-two scale);
@@ -334,9 +346,14 @@ __device__ __forceinline__ bool mass_reached(uint64_t m, uint64_t thq, uint64_t 
 
 __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs a) {
   extern __shared__ uint64_t sel_smem[];
+  const int fs = min(a.P2, kFastSel);
   uint64_t* keys = sel_smem;                                      // [P2]
-  uint64_t* red64 = keys + a.P2;                                  // [2 * 8 waves]
-  uint32_t* mask = reinterpret_cast<uint32_t*>(red64 + 16);       // [nwords]
+  uint64_t* sel = keys + a.P2;                                    // [fs]
+  uint64_t* ordered = sel + fs;                                   // [fs]
+  uint64_t* red64 = ordered + fs;                                 // [2 * 8 waves]
+  SelectCtl* ctl = reinterpret_cast<SelectCtl*>(red64 + 16);
+  int* hist = reinterpret_cast<int*>(ctl + 1);                    // [256]
+  uint32_t* mask = reinterpret_cast<uint32_t*>(hist + 256);       // [nwords]
   int* wscan = reinterpret_cast<int*>(mask + a.nwords);           // [8 waves + 2]
 
   const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x, nt = blockDim.x;
@@ -386,37 +403,113 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     m0 += red64[8 + j];
   }
 
-  // 2. bitonic sort, ascending
-  for (int k = 2; k <= a.P2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int e = t; e < (a.P2 >> 1); e += nt) {
-        const int lo = 2 * e - (e & (j - 1));
-        const int hi = lo + j;
-        const uint64_t x = keys[lo], y = keys[hi];
-        const bool up = (lo & k) == 0;
-        if ((x > y) == up) {
-          keys[lo] = y;
-          keys[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // 3. number of candidates taken after the reservation
+  // caps of this row
   const int K = covered ? a.K_cov : a.K_unc;
   // geometry-only rows take the plain top-K (overlaps are not a distribution)
   const float theta = covered ? (a.mode == 2 ? 1.0f : a.theta_cov) : a.theta_unc;
   const int limit = max(0, min(K - n_res, M - n_res));
+  const bool cut = theta < 1.0f && limit > 0;
+
+  // 2. the `limit` smallest keys, in `top` (ascending when cut)
+  const uint64_t* top = keys;
+  if (limit <= kFastSel) {
+    uint64_t prefix = 0;
+    int shift = 64;
+    if (limit > 0) {
+      int rank = limit - 1;  // rank of the wanted key inside the current bucket
+      for (int pass = 0; pass < 8; ++pass) {
+        shift -= 8;
+        for (int b = t; b < 256; b += nt) hist[b] = 0;
+        __syncthreads();
+        for (int r = t; r < M; r += nt) {
+          const uint64_t key = keys[r];
+          if (shift == 56 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+            atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
+        __syncthreads();
+        if (wv == 0) {  // lane l scans bins 4 l .. 4 l + 3
+          int c4[4], sum = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            c4[q] = hist[4 * lane + q];
+            sum += c4[q];
+          }
+          int incl = sum;
+#pragma unroll
+          for (int o = 1; o < kWave; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (lane >= o) incl += v;
+          }
+          int before = incl - sum;
+          if (before <= rank && rank < incl) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (rank >= before && rank < before + c4[q]) {
+                ctl->prefix = prefix | (static_cast<uint64_t>(4 * lane + q) << shift);
+                ctl->rank = rank - before;
+                ctl->cnt = c4[q];
+              }
+              before += c4[q];
+            }
+          }
+        }
+        __syncthreads();
+        prefix = ctl->prefix;
+        rank = ctl->rank;
+        if (rank == ctl->cnt - 1) break;  // the whole bucket is taken (uniform)
+      }
+    }
+    // gather the keys whose top 64 - shift bits do not exceed the bucket's:
+    // exactly `limit` of them
+    if (t == 0) ctl->n = 0;
+    __syncthreads();
+    if (limit > 0) {
+      for (int r = t; r < M; r += nt) {
+        const uint64_t key = keys[r];
+        if (key != ~0ull && (key >> shift) <= (prefix >> shift)) sel[atomicAdd(&ctl->n, 1)] = key;
+      }
+    }
+    __syncthreads();
+    top = sel;
+    if (cut) {  // ascending order: each key's position is the number of keys below it
+      for (int e = t; e < limit; e += nt) {
+        const uint64_t key = sel[e];
+        int pos = 0;
+        for (int u = 0; u < limit; ++u) pos += sel[u] < key;
+        ordered[pos] = key;
+      }
+      __syncthreads();
+      top = ordered;
+    }
+  } else {
+    // all keys in ascending order (bitonic sort)
+    for (int k = 2; k <= a.P2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int e = t; e < (a.P2 >> 1); e += nt) {
+          const int lo = 2 * e - (e & (j - 1));
+          const int hi = lo + j;
+          const uint64_t x = keys[lo], y = keys[hi];
+          const bool up = (lo & k) == 0;
+          if ((x > y) == up) {
+            keys[lo] = y;
+            keys[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  // 3. number of candidates taken after the reservation
   int c = limit;
-  if (theta < 1.0f && limit > 0) {
+  if (cut) {
     const uint64_t thq = static_cast<uint64_t>(static_cast<double>(theta) * 0x1p24);
     if (t == 0) wscan[nwv] = limit;
     __syncthreads();
     uint64_t carry = m0;
     for (int base = 0; base < limit; base += nt) {
       const int j = base + t;
-      const uint64_t Wj = j < limit ? fixed_mass(key_weight(keys[j])) : 0ull;
+      const uint64_t Wj = j < limit ? fixed_mass(key_weight(top[j])) : 0ull;
       // inclusive scan of Wj over the workgroup
       uint64_t incl = Wj;
 #pragma unroll
@@ -443,7 +536,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   // 4. bitmask: reserved, selected, safeguards
   for (int r = res0 + t; r < M; r += nt) atomicOr(&mask[r >> 5], 1u << (r & 31));
   for (int j = t; j < c; j += nt) {
-    const uint32_t r = static_cast<uint32_t>(keys[j]);
+    const uint32_t r = static_cast<uint32_t>(top[j]);
     atomicOr(&mask[r >> 5], 1u << (r & 31));
   }
   if (a.neigh26) {
@@ -586,8 +679,10 @@ hipError_t launch_route_scores_shared(const void* q, bool bf16, int64_t ld_q_h, 
 
 size_t route_select_lds_bytes(int M) {
   const int P2 = next_pow2(M > 0 ? M : 1);
+  const int fs = P2 < kFastSel ? P2 : kFastSel;
   const int nwords = (M + 31) / 32;
-  return sizeof(uint64_t) * (P2 + 16) + sizeof(uint32_t) * nwords + sizeof(int) * 16;
+  return sizeof(uint64_t) * (P2 + 2 * fs + 16) + sizeof(SelectCtl) + sizeof(int) * 256 +
+         sizeof(uint32_t) * nwords + sizeof(int) * 16;
 }
 
 hipError_t launch_route_select(const float* p, const float* g, const float* rho,
