@@ -22,6 +22,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "velox_device.hpp"
 #include "velox_launch.hpp"
 
@@ -42,6 +44,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sum over aligned groups of G lanes (G = 16 or 8), every lane receiving its
+// group's total: DPP adds within quads, then across quads of the 16-lane row
+// (rotations by 4 and 8) or of the 8-lane half row (mirror).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 16 || G == 8, "group of 8 or 16 lanes");
+  auto add_dpp = [](float x, auto ctrl) {
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false);
+    return x + __int_as_float(y);
+  };
+  v = add_dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  v = add_dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  if constexpr (G == 16) {
+    v = add_dpp(v, std::integral_constant<int, 0x124>{});  // row_ror:4
+    v = add_dpp(v, std::integral_constant<int, 0x128>{});  // row_ror:8
+  } else {
+    v = add_dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  }
   return v;
 }
 
@@ -118,10 +141,14 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x
 // One workgroup (512 threads) per (group of QB query blocks, head).
 //  1. query block means: 16-byte loads, all QB blocks' loads in flight, then a
 //     reduction over row groups in LDS.
-//  2. logits: each thread owns history blocks r = t, t + 512, ...; it streams
-//     kbar[h][r] with 16-byte loads and dots it with the QB query means, which
-//     are broadcast from LDS. Logits of the QB rows stay in LDS.
-//  3. softmax over the history blocks of each row, written coalesced.
+//  2. logits: a group of D / 8 lanes shares each history row (contiguous
+//     16-byte loads of kbar[h][r], several rows in flight); each lane dots its
+//     8 dims with the QB query means held in registers and DPP adds sum the
+//     group. Logits of the QB rows stay in LDS.
+//  3. softmax over the history blocks of each row (all QB rows reduced
+//     together), written coalesced: exp through the hardware exp2 and one
+//     reciprocal per row (within a few float32 ulps of the correctly rounded
+//     values).
 
 constexpr int kScoreThreads = 512;
 
@@ -195,34 +222,60 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     }
   }
 
-  // 2. logits
+  // 2. logits. The lanes of a group of kLpr = D / 8 lanes share one history
+  // row: lane j8 loads its 8 dims (a row is read contiguously by its group)
+  // and dots them with the same 8 dims of every query mean, which it keeps in
+  // registers; DPP adds then sum the group's partials (every lane ends with
+  // the row's dot products). The loads of the next kBatch rows are issued
+  // before the arithmetic of the current ones.
+  constexpr int kLpr = D / 8, kRpw = kWave / kLpr;
+  constexpr int kRowsPerIt = kRpw * (kScoreThreads / kWave);
+  const int lane = t % kWave, wv = t / kWave;
+  const int j8 = lane % kLpr, rg = lane / kLpr;
+  float qv[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + j8 * 8 + e] : 0.f;
   const float* kb = kbar + h * ld_kbar_h;
-  for (int r = t; r < M; r += kScoreThreads) {
-    const float4* krow = reinterpret_cast<const float4*>(kb + static_cast<int64_t>(r) * D);
-    float dot[QB];
+  // rows past the end load the last row (no branch around the loads, so the
+  // compiler can count them); their dot products are not stored
+  auto load_row = [&](int r, float (&x)[8]) {
+    const float4* src =
+        reinterpret_cast<const float4*>(kb + static_cast<int64_t>(min(r, M - 1)) * D + j8 * 8);
+    const float4 u = src[0], v = src[1];
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  };
+  constexpr int kBatch = 4;  // rows per lane group in flight
+  const int r_me = wv * kRpw + rg;
+  float kx[kBatch][8];
+  if (M > 0) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) dot[qb] = 0.f;
-    // not unrolled: keeps the loop-invariant query means in LDS, not registers
-#pragma unroll 1
-    for (int c0 = 0; c0 < D / 4; c0 += 8) {
-      float4 kv[8];
+    for (int b = 0; b < kBatch; ++b) load_row(r_me + b * kRowsPerIt, kx[b]);
+  }
+  for (int r0 = 0; r0 < M; r0 += kBatch * kRowsPerIt) {
+    float nx[kBatch][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kv[u] = krow[c0 + u];
+    for (int b = 0; b < kBatch; ++b) load_row(r0 + (kBatch + b) * kRowsPerIt + r_me, nx[b]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+    for (int b = 0; b < kBatch; ++b) {
+      const int r = r0 + b * kRowsPerIt + r_me;
+      float mine = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float4 qv = reinterpret_cast<const float4*>(qbar + qb * D)[c0 + u];
-          dot[qb] = fmaf(qv.x, kv[u].x, dot[qb]);
-          dot[qb] = fmaf(qv.y, kv[u].y, dot[qb]);
-          dot[qb] = fmaf(qv.z, kv[u].z, dot[qb]);
-          dot[qb] = fmaf(qv.w, kv[u].w, dot[qb]);
-        }
+      for (int qb = 0; qb < QB; ++qb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(qv[qb][e], kx[b][e], acc);
+        acc = group_sum<kLpr>(acc);
+        if (j8 == qb) mine = acc;
       }
+      if (r < M && j8 < nq) logit[j8 * M + r] = mine * scale;
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      if (qb < nq) logit[qb * M + r] = dot[qb] * scale;
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kx[b][e] = nx[b][e];
   }
   __syncthreads();
 
@@ -234,21 +287,50 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     return;
   }
 
-  // 3. softmax over the history blocks of each row
-  for (int qb = 0; qb < nq; ++qb) {
-    float* lr = logit + qb * M;
-    float mx = -INFINITY;
-    for (int r = t; r < M; r += kScoreThreads) mx = fmaxf(mx, lr[r]);
-    mx = block_max(mx, red);
-    float sum = 0.f;
-    for (int r = t; r < M; r += kScoreThreads) {
-      const float e = expf(lr[r] - mx);
-      lr[r] = e;
-      sum += e;
+  // 3. softmax over the history blocks of each row, all rows at once: maxima,
+  // then exponentials and sums, then the normalised values written coalesced
+  // (`red` is free again and holds the per-wave partials)
+  constexpr int kWaves = kScoreThreads / kWave;
+  float mx[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mx[qb] = -INFINITY;
+    if (qb < nq)
+      for (int r = t; r < M; r += kScoreThreads) mx[qb] = fmaxf(mx[qb], logit[qb * M + r]);
+    mx[qb] = wave_max(mx[qb]);
+    if (lane == 0) red[qb * kWaves + wv] = mx[qb];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float m = red[qb * kWaves];
+    for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, red[qb * kWaves + w2]);
+    mx[qb] = m;
+  }
+  __syncthreads();
+  float sm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    sm[qb] = 0.f;
+    if (qb < nq) {
+      float* lr = logit + qb * M;
+      for (int r = t; r < M; r += kScoreThreads) {
+        const float e = __expf(lr[r] - mx[qb]);
+        lr[r] = e;
+        sm[qb] += e;
+      }
     }
-    sum = block_sum(sum, red);
+    sm[qb] = wave_sum(sm[qb]);
+    if (lane == 0) red[qb * kWaves + wv] = sm[qb];
+  }
+  __syncthreads();
+  for (int qb = 0; qb < nq; ++qb) {
+    float sum = red[qb * kWaves];
+    for (int w2 = 1; w2 < kWaves; ++w2) sum += red[qb * kWaves + w2];
+    const float inv = 1.0f / sum;
+    const float* lr = logit + qb * M;
     float* out = p + (static_cast<int64_t>(h) * N + i0 + qb) * M;
-    for (int r = t; r < M; r += kScoreThreads) out[r] = lr[r] / sum;
+    for (int r = t; r < M; r += kScoreThreads) out[r] = lr[r] * inv;
   }
 }
 
