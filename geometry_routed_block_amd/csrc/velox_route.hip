@@ -31,15 +31,29 @@ namespace velox {
 
 // ---------------------------------------------------------------- reductions
 
+// Wave-wide all-reduce without LDS: DPP within quads and 16-lane rows, then
+// the row and half-wave swaps (every lane ends with the result). Called with
+// all 64 lanes active.
+template <typename Op>
+__device__ __forceinline__ float wave_allreduce(float v, float identity, Op op) {
+  auto dpp = [&](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x),
+                                                      decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  v = op(v, dpp(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_allreduce(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_allreduce(v, 0.f, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
@@ -176,7 +190,7 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
 template <typename T, int D, int QB, bool kRaw = false>
 __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     const T* __restrict__ q, int64_t ld_q_h, const float* __restrict__ kbar, int64_t ld_kbar_h,
-    int N, int M, float scale, float* __restrict__ p) {
+    int H, int N, int M, float scale, float* __restrict__ p) {
   constexpr int kCpr = D / 8;                      // 8-element chunks per token row
   constexpr int kGroups = kScoreThreads / kCpr;    // token-row groups
   constexpr int kPasses = kBlock / kGroups;
@@ -184,7 +198,11 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   float* qbar = smem;                              // [QB][D]
   float* red = qbar + QB * D;                      // [kGroups][D]
   float* logit = red + kGroups * D;                // [QB][M]
-  const int h = blockIdx.y, i0 = blockIdx.x * QB, t = threadIdx.x;
+  // one-dimensional grid of H * groups workgroups, remapped so that the
+  // groups of a head share an XCD (its kbar rows are read once into that L2)
+  const int groups = (N + QB - 1) / QB;
+  const int wg = xcd_remap(blockIdx.x, H * groups);
+  const int h = wg / groups, i0 = (wg % groups) * QB, t = threadIdx.x;
   const int nq = min(QB, N - i0);
 
   // 1. query block means, two blocks' loads in flight at a time
@@ -707,9 +725,9 @@ static hipError_t scores_launch(const void* q, int64_t ld_q_h, const float* kbar
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  dim3 grid((N + QB - 1) / QB, H);
+  dim3 grid(((N + QB - 1) / QB) * H);
   hipLaunchKernelGGL(kern, grid, dim3(kScoreThreads), lds, stream, static_cast<const T*>(q),
-                     ld_q_h, kbar, ld_kbar_h, N, M, scale, p);
+                     ld_q_h, kbar, ld_kbar_h, H, N, M, scale, p);
   return hipGetLastError();
 }
 
