@@ -63,7 +63,76 @@ def parse():
                          "known-size reference for HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the sparse-attention part of the oracle sample")
+    ap.add_argument("--trace", type=str, default="",
+                    help="comma-separated chunk numbers of the 48-chunk rollout (e.g. 1,2,4,8,16,32,48): "
+                         "instead of the chunk-48 step, time the routed step and dense attention at "
+                         "each chunk (one layer, 40 heads) and print the latency-vs-chunk curve")
     return ap.parse_args()
+
+
+def run_trace(args):
+    """Latency of the routed step (importance, routes, sparse attention) and of
+    dense attention along the rollout: chunk c has 36 (c - 1) history blocks."""
+    import numpy as np
+    import torch
+
+    import geometry_routed_block_amd as velox
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    chunks = [int(c) for c in args.trace.split(",") if c.strip()]
+    if not chunks or min(chunks) < 1 or max(chunks) > 48:
+        raise SystemExit("--trace takes chunk numbers in 1..48")
+    rows = []
+
+    def timed(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for c in chunks:
+        wl = synth.trace_chunk(c, layer=0)
+        q, k, v = synth.make_qkv(wl, device=dev)
+        M = wl.M
+        kbar = velox.block_mean(k[:, : M * 128]) if M > 0 else None
+        g = torch.from_numpy(wl.g).to(dev)
+        rho = torch.from_numpy(wl.rho).to(dev)
+        coord = torch.from_numpy(np.ascontiguousarray(wl.coords, np.int32)).to(dev)
+        L = velox.route_bound(wl.params, M)
+        p = torch.zeros(wl.H, wl.N, M, dtype=torch.float32, device=dev)
+        ids = torch.empty(wl.H, wl.N, max(L, 1), dtype=torch.int32, device=dev)
+        lens = torch.empty(wl.H, wl.N, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        od = torch.empty_like(q)
+
+        def step():
+            if M > 0:
+                velox.route_scores(q, kbar, M, out=p)
+            velox.route_select(p, g, rho, coord, wl.params, L=max(L, 1), route_ids=ids, route_len=lens)
+            velox.sparse_attn(q, k, v, ids, lens, M, out=o)
+
+        routed = timed(step, args.warmup, args.steps)
+        dense = timed(lambda: velox.dense_attn(q, k, v, M, out=od), 1, max(args.dense_steps, 1))
+        tiles = int((lens.cpu().numpy() + wl.N).sum())
+        rows.append({"chunk": c, "M": M, "routed_ms": round(routed, 4), "dense_ms": round(dense, 4),
+                     "speedup": round(dense / routed, 3), "tiles_visited": tiles})
+        log(f"chunk {c:2d} M={M:4d}: routed {routed:.3f} ms, dense {dense:.3f} ms ({dense / routed:.2f}x)")
+        del q, k, v, kbar, o, od
+        torch.cuda.empty_cache()
+    cross = next((r["chunk"] for r in rows if r["routed_ms"] < r["dense_ms"]), None)
+    print(json.dumps({"metric": "routed step vs dense attention latency per call along the 48-chunk rollout",
+                      "unit": "ms", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "48-chunk rollout trace: one layer (seed 1000), 40 heads, d 128, "
+                                             "36 query blocks, 36 (c - 1) history blocks at chunk c"},
+                      "first_chunk_routed_faster": cross, "trace": rows}), flush=True)
 
 
 def unique_tile_count(ids, lens, N, M):
@@ -142,6 +211,10 @@ def main():
               "(the path is single-GPU; multi-GPU sharding is a design note only)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.trace:
+        run_trace(args)
+        return
 
     import numpy as np
     import torch
