@@ -67,6 +67,9 @@ def parse():
                     help="comma-separated chunk numbers of the 48-chunk rollout (e.g. 1,2,4,8,16,32,48): "
                          "instead of the chunk-48 step, time the routed step and dense attention at "
                          "each chunk (one layer, 40 heads) and print the latency-vs-chunk curve")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the chunk-48 step, time the routed step and dense attention at the "
+                         "chunk-48 shape with 0%%, 50%% and 100%% of the query blocks covered")
     return ap.parse_args()
 
 
@@ -81,9 +84,13 @@ def run_trace(args):
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    chunks = [int(c) for c in args.trace.split(",") if c.strip()]
-    if not chunks or min(chunks) < 1 or max(chunks) > 48:
-        raise SystemExit("--trace takes chunk numbers in 1..48")
+    if args.sweep:
+        cases = [(f"covered {int(f * 100)}%", (lambda f=f: synth.sweep(f))) for f in (0.0, 0.5, 1.0)]
+    else:
+        chunks = [int(c) for c in args.trace.split(",") if c.strip()]
+        if not chunks or min(chunks) < 1 or max(chunks) > 48:
+            raise SystemExit("--trace takes chunk numbers in 1..48")
+        cases = [(c, (lambda c=c: synth.trace_chunk(c, layer=0))) for c in chunks]
     rows = []
 
     def timed(fn, warm, reps):
@@ -98,8 +105,8 @@ def run_trace(args):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    for c in chunks:
-        wl = synth.trace_chunk(c, layer=0)
+    for c, make in cases:
+        wl = make()
         q, k, v = synth.make_qkv(wl, device=dev)
         M = wl.M
         kbar = velox.block_mean(k[:, : M * 128]) if M > 0 else None
@@ -122,11 +129,18 @@ def run_trace(args):
         routed = timed(step, args.warmup, args.steps)
         dense = timed(lambda: velox.dense_attn(q, k, v, M, out=od), 1, max(args.dense_steps, 1))
         tiles = int((lens.cpu().numpy() + wl.N).sum())
-        rows.append({"chunk": c, "M": M, "routed_ms": round(routed, 4), "dense_ms": round(dense, 4),
+        rows.append({("covered" if args.sweep else "chunk"): c, "M": M, "routed_ms": round(routed, 4), "dense_ms": round(dense, 4),
                      "speedup": round(dense / routed, 3), "tiles_visited": tiles})
-        log(f"chunk {c:2d} M={M:4d}: routed {routed:.3f} ms, dense {dense:.3f} ms ({dense / routed:.2f}x)")
+        log(f"{c}: M={M:4d}: routed {routed:.3f} ms, dense {dense:.3f} ms ({dense / routed:.2f}x), "
+            f"{tiles} tiles")
         del q, k, v, kbar, o, od
         torch.cuda.empty_cache()
+    if args.sweep:
+        print(json.dumps({"metric": "routed step vs dense attention latency per call at the chunk-48 shape "
+                                    "by covered fraction", "unit": "ms", "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": "chunk-48 coverage sweep (seeds 480-482)"},
+                          "sweep": rows}), flush=True)
+        return
     cross = next((r["chunk"] for r in rows if r["routed_ms"] < r["dense_ms"]), None)
     print(json.dumps({"metric": "routed step vs dense attention latency per call along the 48-chunk rollout",
                       "unit": "ms", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
@@ -212,7 +226,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.trace:
+    if args.trace or args.sweep:
         run_trace(args)
         return
 
