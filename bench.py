@@ -390,6 +390,29 @@ def main():
                                "tiles_visited": int((lens_sh.cpu().numpy() + wl.N).sum()) * wl.H}
     log(f"variants: {variants}")
 
+    # one GPU's share of the heads under head parallelism (5 of 40 heads, the
+    # chunk-48 rows of those heads): 90 workgroups for 256 CUs unless each
+    # row's tiles are split over several workgroups
+    wl5 = synth.chunk48(heads=5)
+    q5, k5, v5 = synth.make_qkv(wl5, device=dev)
+    kbar5 = velox.block_mean(k5[:, : wl5.M * 128])
+    p5 = velox.route_scores(q5, kbar5, wl5.M)
+    ids5, lens5 = velox.route_select(p5, g, rho, coord, wl5.params, L=L)
+    o5 = torch.empty_like(q5)
+    share = {"heads": 5, "tiles_visited": int((lens5.cpu().numpy() + wl5.N).sum()), "sparse_ms": {},
+             "dense_ms": {}}
+    for n in (1, 2, 4, 8):
+        ws5 = velox.split_workspace(q5, n) if n > 1 else None
+        share["sparse_ms"][n] = round(timed(lambda: velox.sparse_attn(q5, k5, v5, ids5, lens5, wl5.M, out=o5,
+                                                                      n_split=n, workspace=ws5)), 4)
+        share["dense_ms"][n] = round(timed(lambda: velox.dense_attn(q5, k5, v5, wl5.M, out=o5, n_split=n,
+                                                                    workspace=ws5)), 4)
+    best = min(share["sparse_ms"], key=share["sparse_ms"].get)
+    share["sparse_tflops_best"] = round(4.0 * 128 ** 2 * wl5.d * share["tiles_visited"]
+                                        / (share["sparse_ms"][best] * 1e-3) / 1e12, 1)
+    log(f"one GPU's share (5 heads): {share}")
+    del q5, k5, v5, kbar5, p5, o5
+
     # KV append of one chunk in global order (once per chunk per layer, at
     # model QKV time: reported beside the step). 3 latent frames of 32 x 48
     # tokens = the 36 blocks of a chunk, written over the current chunk's rows
@@ -455,6 +478,7 @@ def main():
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
         "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
         "router_variants": variants,
+        "head_share_split_rows": share,
         "geometry_ms": geo_ms,
         "kv_append": {"ms": round(append_ms, 4), "bytes": append_bytes,
                       "gbps": round(append_bytes / append_ms / 1e6, 1),

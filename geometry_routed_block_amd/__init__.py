@@ -30,7 +30,7 @@ from ._lib import VELOX_BLOCK, VeloxError
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
            "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
            "gilbert_curve", "kv_append", "route_scores_shared", "slab_table", "multiwarp",
-           "token_points", "library_path"]
+           "token_points", "library_path", "split_workspace"]
 
 
 def library_path() -> str:
@@ -201,12 +201,33 @@ def _attn_out(q, out, lse, want_lse):
     return out, lse
 
 
+def split_workspace(q, n_split: int):
+    """A device workspace for the split-row attention calls (uint8 tensor)."""
+    torch = _torch()
+    H, NT, _ = q.shape
+    nbytes = _lib.load().velox_attn_split_workspace_size(H, NT // VELOX_BLOCK, int(n_split))
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=q.device)
+
+
+def _split_args(q, n_split, workspace):
+    if n_split == 1:
+        return None, 0
+    if workspace is None:
+        workspace = split_workspace(q, n_split)
+    _require_cuda(workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = True,
-                scale: float | None = None, out=None, lse=None, want_lse: bool = False):
+                scale: float | None = None, out=None, lse=None, want_lse: bool = False,
+                n_split: int = 1, workspace=None):
     """Attention of each query block over its routed history tiles (+ current chunk).
 
     route_ids [H][N][L] / route_len [H][N] give one route per head; [N][L] / [N]
     (or [1][N][L] / [1][N]) one route per query block shared by all heads.
+    n_split > 1 cuts every row's tiles into that many ranges (per-head routes
+    only); `workspace` is then a device buffer of split_workspace(q, n_split)'s
+    size (allocated here when None).
     """
     _require_cuda(q, k, v, route_ids, route_len)
     H, NT, d = q.shape
@@ -221,6 +242,16 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
     if route_len.numel() not in (N, H * N) or route_ids.numel() != route_len.numel() * route_ids.shape[-1]:
         raise ValueError("routes must be [H][N][L] + [H][N] (per head) or [N][L] + [N] (shared)")
     shared = route_len.numel() != H * N
+    if n_split != 1:
+        if shared:
+            raise ValueError("split rows take per-head routes")
+        ws, ws_bytes = _split_args(q, n_split, workspace)
+        _lib.check(lib.velox_sparse_attn_split(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), _rows(q, "q"), _rows(k, "k"),
+            H, N, M, d, ctypes.c_float(scale), route_ids.data_ptr(), route_len.data_ptr(),
+            route_ids.shape[-1], 1 if include_current else 0, int(n_split), ws.data_ptr(), ws_bytes,
+            out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q)))
+        return (out, lse) if want_lse or lse is not None else out
     fn = lib.velox_sparse_attn_shared if shared else lib.velox_sparse_attn
     _lib.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), _rows(q, "q"),
                   _rows(k, "k"), H, N, M, d, ctypes.c_float(scale), route_ids.data_ptr(),
@@ -230,8 +261,9 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
 
 
 def dense_attn(q, k, v, M: int, scale: float | None = None, out=None, lse=None,
-               want_lse: bool = False):
-    """Dense baseline: every history tile and every current-chunk tile."""
+               want_lse: bool = False, n_split: int = 1, workspace=None):
+    """Dense baseline: every history tile and every current-chunk tile
+    (n_split / workspace as for sparse_attn)."""
     _require_cuda(q, k, v)
     H, NT, d = q.shape
     N = NT // VELOX_BLOCK
@@ -240,6 +272,14 @@ def dense_attn(q, k, v, M: int, scale: float | None = None, out=None, lse=None,
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
     lib = _lib.load()
+    if n_split != 1:
+        ws, ws_bytes = _split_args(q, n_split, workspace)
+        _lib.check(lib.velox_dense_attn_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                              _rows(q, "q"), _rows(k, "k"), H, N, M, d,
+                                              ctypes.c_float(scale), int(n_split), ws.data_ptr(),
+                                              ws_bytes, out.data_ptr(),
+                                              lse.data_ptr() if lse is not None else None, _stream(q)))
+        return (out, lse) if want_lse or lse is not None else out
     _lib.check(lib.velox_dense_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
                                     _rows(q, "q"), _rows(k, "k"), H, N, M, d,
                                     ctypes.c_float(scale), out.data_ptr(),

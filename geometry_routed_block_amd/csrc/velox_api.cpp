@@ -187,11 +187,36 @@ velox_status_t velox_route_select(const float* p, const float* g, const float* r
                   "velox_route_select");
 }
 
+size_t velox_attn_split_workspace_size(int H, int N, int n_split) {
+  if (H < 1 || N < 1 || n_split < 1) return 0;
+  const size_t rows = static_cast<size_t>(n_split) * H * N * VELOX_BLOCK;
+  return rows * (128 + 2) * sizeof(float);
+}
+
+// Split settings into the launch config: the workspace holds part_o
+// [n_split][rows][128] then part_ml [n_split][rows][2].
+static velox_status_t set_split(velox::AttnConfig& c, int n_split, void* workspace,
+                                size_t workspace_bytes) {
+  REQUIRE(n_split >= 1 && n_split <= VELOX_MAX_SPLIT, "n_split must be in [1, %d] (got %d)",
+          VELOX_MAX_SPLIT, n_split);
+  c.n_split = n_split;
+  if (n_split == 1) return VELOX_OK;
+  const size_t need = velox_attn_split_workspace_size(c.H, c.N, n_split);
+  REQUIRE(workspace, "workspace must be non-NULL when n_split > 1");
+  REQUIRE(workspace_bytes >= need, "workspace of %zu bytes is smaller than the %zu needed",
+          workspace_bytes, need);
+  REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 16 == 0, "workspace must be 16-byte aligned");
+  c.part_o = static_cast<float*>(workspace);
+  c.part_ml = c.part_o + static_cast<size_t>(n_split) * c.H * c.N * VELOX_BLOCK * 128;
+  return VELOX_OK;
+}
+
 static velox_status_t sparse_common(const void* q, const void* k, const void* v, velox_dtype_t dt,
                                     int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
                                     float scale, const int32_t* route_ids, const int32_t* route_len,
                                     int L, int include_current, void* o, float* lse, void* stream,
-                                    bool shared, const char* what) {
+                                    bool shared, const char* what, int n_split = 1,
+                                    void* workspace = nullptr, size_t workspace_bytes = 0) {
   velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
   if (st != VELOX_OK) return st;
   REQUIRE(route_ids && route_len, "route_ids and route_len must be non-NULL");
@@ -199,6 +224,8 @@ static velox_status_t sparse_common(const void* q, const void* k, const void* v,
   REQUIRE(include_current == 0 || include_current == 1, "include_current must be 0 or 1");
   velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
                       route_ids, route_len, L, shared, include_current, o, lse};
+  st = set_split(c, n_split, workspace, workspace_bytes);
+  if (st != VELOX_OK) return st;
   return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -219,14 +246,45 @@ velox_status_t velox_sparse_attn_shared(const void* q, const void* k, const void
                        include_current, o, lse, stream, true, "velox_sparse_attn_shared");
 }
 
-velox_status_t velox_dense_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
-                                int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
-                                float scale, void* o, float* lse, void* stream) {
+static velox_status_t dense_common(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                                   int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                                   float scale, void* o, float* lse, void* stream, const char* what,
+                                   int n_split = 1, void* workspace = nullptr,
+                                   size_t workspace_bytes = 0) {
   velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
   if (st != VELOX_OK) return st;
   velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
                       nullptr, nullptr, 0, false, 1, o, lse};
-  return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), "velox_dense_attn");
+  st = set_split(c, n_split, workspace, workspace_bytes);
+  if (st != VELOX_OK) return st;
+  return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), what);
+}
+
+velox_status_t velox_dense_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
+                                int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
+                                float scale, void* o, float* lse, void* stream) {
+  return dense_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o, lse, stream,
+                      "velox_dense_attn");
+}
+
+velox_status_t velox_sparse_attn_split(const void* q, const void* k, const void* v,
+                                       velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                       int N, int M, int d, float scale,
+                                       const int32_t* route_ids, const int32_t* route_len, int L,
+                                       int include_current, int n_split, void* workspace,
+                                       size_t workspace_bytes, void* o, float* lse, void* stream) {
+  return sparse_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, route_ids, route_len, L,
+                       include_current, o, lse, stream, false, "velox_sparse_attn_split", n_split,
+                       workspace, workspace_bytes);
+}
+
+velox_status_t velox_dense_attn_split(const void* q, const void* k, const void* v,
+                                      velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                      int N, int M, int d, float scale, int n_split,
+                                      void* workspace, size_t workspace_bytes, void* o,
+                                      float* lse, void* stream) {
+  return dense_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o, lse, stream,
+                      "velox_dense_attn_split", n_split, workspace, workspace_bytes);
 }
 
 velox_status_t velox_slab_overlap(const float* q_obb, const float* h_obb, int N, int M,

@@ -58,6 +58,14 @@ struct AttnArgs {
   int include_current;
   void* o;
   float* lse;
+  // Split rows (d = 128 bf16 kernel only): n_split > 1 cuts the tile list of
+  // every row into n_split consecutive ranges, one workgroup each; the ranges
+  // leave unnormalised fp32 O in part_o [n_split][H][N*128][128] and the
+  // (max, sum) of their softmax in part_ml [n_split][H][N*128][2], which the
+  // merge kernel combines.
+  int n_split;
+  float* part_o;
+  float* part_ml;
 };
 
 // Route row of (head h, query block i).
@@ -541,8 +549,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int grp = lane / 16, gi = lane % 16;
   const int N = a.N, M = a.M;
   const int pairs = (N + 1) / 2;
-  const int G = (a.G / N) * pairs;
-  // ---- which (head, pair) this workgroup serves. A pair is two rows of one
+  const int nsp = max(a.n_split, 1);
+  const int G = (a.G / N) * pairs * nsp;  // work units: (head, pair, range)
+  // ---- which (head, pair, range) this workgroup serves. A pair is two rows of one
   // head, ranks 2 pr and 2 pr + 1 of its rows ordered by route length (longest
   // first, ties by index). Each XCD owns a contiguous range of (head, pair) ids
   // (xcd_remap). Routed: the XCD's workgroups, in dispatch order, take that
@@ -550,18 +559,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // short pairs fill the tail of the grid); the order is computed here from the
   // route lengths, staged in route_lds before the route ids use it.
   int* lens_s = &route_lds[0][0];
-  int h, pr;
+  int h, pr, split;
   if (t < 2) pair_rows[t] = -1;
   if (kRouted) {
     const int x = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
     int base, cnt;
     xcd_range(x, G, base, cnt);
-    const int h_lo = base / pairs, nh = (base + cnt - 1) / pairs - h_lo + 1;
+    const int h_lo = base / nsp / pairs, nh = (base + cnt - 1) / nsp / pairs - h_lo + 1;
     const int nr = nh * N;
     int* rank_s = lens_s + nr;
     int* cost_s = rank_s + nr;
     int* sorted_s = cost_s + cnt;
-    if (4 * nr <= 2 * kMaxRoute && cnt <= nr) {
+    if (3 * nr + cnt <= 2 * kMaxRoute) {
       for (int e = t; e < nr; e += kThreads)
         lens_s[e] = min(max(a.route_len[route_row(a, h_lo + e / N, e % N)], 0), a.L);
       __syncthreads();
@@ -574,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       }
       __syncthreads();
       for (int w = t; w < cnt; w += kThreads) {
-        const int id = base + w;
+        const int id = (base + w) / nsp;  // (head, pair) of the unit
         cost_s[w] = sorted_s[(id / pairs - h_lo) * N + 2 * (id % pairs)];
       }
       __syncthreads();
@@ -586,8 +595,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       }
       __syncthreads();
       const int wg = pair_rows[0];
-      h = wg / pairs;
-      pr = wg % pairs;
+      split = wg % nsp;
+      h = wg / nsp / pairs;
+      pr = wg / nsp % pairs;
       __syncthreads();
       if (t < 2) pair_rows[t] = -1;
       __syncthreads();
@@ -598,8 +608,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     } else {
       // too many rows to stage: dispatch order of the logical ids
       const int wg = xcd_remap(blockIdx.x, G);
-      h = wg / pairs;
-      pr = wg % pairs;
+      split = wg % nsp;
+      h = wg / nsp / pairs;
+      pr = wg / nsp % pairs;
       __syncthreads();
       for (int r = t; r < N; r += kThreads) {
         const int* lens = a.route_len + route_row(a, h, 0);
@@ -614,8 +625,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     }
   } else {
     const int wg = xcd_remap(blockIdx.x, G);
-    h = wg / pairs;
-    pr = wg % pairs;
+    split = wg % nsp;
+    h = wg / nsp / pairs;
+    pr = wg / nsp % pairs;
     __syncthreads();
     for (int r = t; r < N; r += kThreads)
       if (r / 2 == pr) pair_rows[r & 1] = r;
@@ -631,7 +643,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     if (kRouted) rlen = M == 0 ? 0 : min(max(a.route_len[route_row(a, h, i)], 0), a.L);
     ncur = (!kRouted || a.include_current) ? N : 0;
   }
-  const int S = 2 * (rlen + ncur);     // half-tiles of this team's row
+  // this unit's range [t0, t1) of the row's tile list (the whole list unless
+  // rows are split)
+  const int t_row = rlen + ncur;
+  const int t_chunk = (t_row + nsp - 1) / nsp;
+  const int t0 = min(t_row, split * t_chunk);
+  const int S = 2 * (min(t_row, t0 + t_chunk) - t0);  // half-tiles of this team's range
   if (kRouted && i >= 0) {
     const int32_t* route = a.route_ids + route_row(a, h, i) * a.L;
     for (int e = t - team * 256; e < rlen; e += 256) route_lds[team][e] = min(max(route[e], 0), M - 1);
@@ -694,11 +711,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // inside route_lds, so no branch surrounds the read); half_off selects and
   // scales. j may pass the end of the row by two: the result is then unused.
   auto route_raw = [&](int j) {
-    const int e = min(max((j >> 1) - ncur, 0), kMaxRoute - 1);
+    const int e = min(max((j >> 1) + t0 - ncur, 0), kMaxRoute - 1);
     return kRouted ? route_lds[team][e] : 0;
   };
   auto half_off = [&](int j, int id) -> uint64_t {
-    const int jt = j >> 1;
+    const int jt = (j >> 1) + t0;
     const int tile = jt < ncur ? M + jt : (kRouted ? id : jt - ncur);
     return static_cast<uint64_t>(static_cast<uint32_t>(tile)) * (kBlock * D * 2) + (j & 1) * (kHalf * D * 2);
   };
@@ -864,6 +881,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   for (; k < phases; ++k) barrier_nofence();
 
   if (i < 0) return;
+  if (nsp > 1) {  // split rows: this range's unnormalised O and its (max, sum)
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const int64_t prow = (static_cast<int64_t>(split) * (a.G / N) + h) * N * kBlock + qrow;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(po + db * 32 + g4 * 8 + hh * 4) =
+            S == 0 ? make_float4(0.f, 0.f, 0.f, 0.f)
+                   : make_float4(o_acc[db][g4 * 4 + 0], o_acc[db][g4 * 4 + 1], o_acc[db][g4 * 4 + 2],
+                                 o_acc[db][g4 * 4 + 3]);
+    if (hh == 0) {
+      a.part_ml[prow * 2] = S == 0 ? -INFINITY : m_ref;
+      a.part_ml[prow * 2 + 1] = S == 0 ? 0.f : l_tot;
+    }
+    return;
+  }
   // ---- normalise and store
   bf16_t* orow = static_cast<bf16_t*>(a.o) + (static_cast<int64_t>(h) * N * kBlock + qrow) * D;
   if (S == 0) {
@@ -893,6 +928,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
 }
 
 }  // namespace pp
+
+// Combines the n_split ranges of every query row (four threads per row, 32
+// dims each): m = max m_s, l = sum of 2^(m_s - m) l_s, O = sum of
+// 2^(m_s - m) O_s / l, lse = m ln 2 + ln l; a row without any tile gets O = 0
+// and lse = -inf. rows = H * N * 128, in the layout of o and lse.
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml, int n_split,
+                                                          int64_t rows, bf16_t* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid >> 2;
+  const int quarter = static_cast<int>(gid & 3);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < n_split; ++s) m = fmaxf(m, part_ml[(s * rows + row) * 2]);
+  float l = 0.f, acc[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float ms = part_ml[(s * rows + row) * 2];
+      if (ms == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - m);
+      l += w * part_ml[(s * rows + row) * 2 + 1];
+      const float4* src = reinterpret_cast<const float4*>(part_o + (s * rows + row) * 128 + quarter * 32);
+#pragma unroll
+      for (int e4 = 0; e4 < 8; ++e4) {
+        const float4 x = src[e4];
+        acc[4 * e4 + 0] += w * x.x;
+        acc[4 * e4 + 1] += w * x.y;
+        acc[4 * e4 + 2] += w * x.z;
+        acc[4 * e4 + 3] += w * x.w;
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(o + row * 128 + quarter * 32);
+#pragma unroll
+  for (int e2 = 0; e2 < 16; ++e2)
+    dst[e2] = static_cast<uint32_t>(f32_to_bf16(acc[2 * e2] * inv)) |
+              (static_cast<uint32_t>(f32_to_bf16(acc[2 * e2 + 1] * inv)) << 16);
+  if (lse && quarter == 0) lse[row] = l > 0.f ? m * 0.6931471805599453f + logf(l) : -INFINITY;
+}
 
 // ---------------------------------------------------------------- fp32
 //
@@ -974,8 +1052,16 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
   // padded tiles staged through registers.
   if (bf16 && D == 128 && (!kRouted || args.L <= pp::kMaxRoute)) {
     const int pairs = (args.N + 1) / 2;
-    hipLaunchKernelGGL((pp::attn_kernel<kRouted>), dim3((args.G / args.N) * pairs), dim3(pp::kThreads),
-                       0, stream, args);
+    const int nsp = args.n_split > 1 ? args.n_split : 1;
+    hipLaunchKernelGGL((pp::attn_kernel<kRouted>), dim3((args.G / args.N) * pairs * nsp),
+                       dim3(pp::kThreads), 0, stream, args);
+    if (nsp > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t rows = static_cast<int64_t>(args.G) * kBlock;
+      hipLaunchKernelGGL(split_merge_kernel, dim3(static_cast<unsigned>((rows * 4 + 255) / 256)), dim3(256), 0,
+                         stream, args.part_o, args.part_ml, nsp, rows, static_cast<bf16_t*>(args.o), args.lse);
+    }
     return hipGetLastError();
   }
   const bool fast = D == 128 && (!kRouted || args.L <= kMaxRouteLds);
@@ -1009,6 +1095,11 @@ hipError_t launch_attention(const AttnConfig& c, hipStream_t stream) {
   a.o = c.o;
   a.lse = c.lse;
   const bool routed = c.route_ids != nullptr;
+  // rows are split only in the d = 128 bf16 kernel; elsewhere n_split is ignored
+  const bool pp_path = c.bf16 && c.d == 128 && (!routed || c.L <= pp::kMaxRoute);
+  a.n_split = pp_path && c.n_split > 1 ? c.n_split : 1;
+  a.part_o = c.part_o;
+  a.part_ml = c.part_ml;
   if (c.d == 128)
     return routed ? launch_one<128, true>(a, c.bf16, stream) : launch_one<128, false>(a, c.bf16, stream);
   return routed ? launch_one<64, true>(a, c.bf16, stream) : launch_one<64, false>(a, c.bf16, stream);

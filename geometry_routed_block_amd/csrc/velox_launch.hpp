@@ -31,6 +31,9 @@ struct AttnConfig {
   int include_current;
   void* o;
   float* lse;
+  int n_split;               // > 1: split rows (d = 128 bf16 only), with the two buffers below
+  float* part_o;             // [n_split][H][N*128][128] fp32
+  float* part_ml;            // [n_split][H][N*128][2] fp32
 };
 
 hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, int nblk, int d,

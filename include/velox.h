@@ -212,6 +212,42 @@ velox_status_t velox_dense_attn(const void* q, const void* k, const void* v,
                                 void* stream);
 
 /*
+ * Split rows: velox_sparse_attn_split and velox_dense_attn_split compute the
+ * same attention as velox_sparse_attn / velox_dense_attn ([digest] Core
+ * method, eq. 15); the difference is only the work distribution. The tile list
+ * of every query row (current chunk, then the routed tiles) is cut into
+ * n_split consecutive ranges, each handled by its own workgroup; the ranges'
+ * unnormalised outputs and softmax (max, sum) go to the workspace and a second
+ * kernel merges them (softmax is associative under rescaling). Meant for
+ * shapes with few rows per GPU, e.g. one GPU's share of the heads (5 heads x 36
+ * query blocks = 180 rows for 256 CUs). Results equal the unsplit call's up to
+ * float rounding.
+ *   n_split          1 .. VELOX_MAX_SPLIT; 1 is the unsplit call
+ *   workspace        device buffer, 16-byte aligned, of at least
+ *                    velox_attn_split_workspace_size(H, N, n_split) bytes,
+ *                    caller-owned; contents undefined on return; may be NULL
+ *                    when n_split = 1
+ *   workspace_bytes  its size
+ * Other arguments as for the unsplit calls. Rows are split only by the d = 128
+ * bf16 kernel with routes of at most 2048 tiles; other shapes run unsplit and
+ * leave the workspace untouched. Two calls that share a workspace must not
+ * overlap in time.
+ */
+#define VELOX_MAX_SPLIT 16
+size_t velox_attn_split_workspace_size(int H, int N, int n_split);
+velox_status_t velox_sparse_attn_split(const void* q, const void* k, const void* v,
+                                       velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                       int N, int M, int d, float scale,
+                                       const int32_t* route_ids, const int32_t* route_len, int L,
+                                       int include_current, int n_split, void* workspace,
+                                       size_t workspace_bytes, void* o, float* lse, void* stream);
+velox_status_t velox_dense_attn_split(const void* q, const void* k, const void* v,
+                                      velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                      int N, int M, int d, float scale, int n_split,
+                                      void* workspace, size_t workspace_bytes, void* o,
+                                      float* lse, void* stream);
+
+/*
  * velox_sparse_attn_shared — velox_sparse_attn with one route per query block
  * shared by every head (routes of velox_route_scores_shared):
  *   route_ids  [N][L] int32, route_len [N] int32

@@ -108,6 +108,30 @@ def test_attention_validation(lib):
     assert de(None, A, A, 1, ldq, ldkv, H, N, M, d, s, A, None, None) == _lib.VELOX_ERR_INVALID
 
 
+def test_split_attention_validation(lib):
+    sp, de = lib.velox_sparse_attn_split, lib.velox_dense_attn_split
+    H, N, M, d = 2, 4, 16, 128
+    ldq, ldkv = N * 128 * d, (M + N) * 128 * d
+    s = ctypes.c_float(0.125)
+    A = 0x10000  # aligned fake pointer
+    need = lib.velox_attn_split_workspace_size(H, N, 3)
+    assert need == 3 * H * N * 128 * 130 * 4
+    assert lib.velox_attn_split_workspace_size(0, N, 3) == 0
+    bad = [
+        (0, A, need),                                 # n_split out of range
+        (_lib.VELOX_MAX_SPLIT + 1, A, 1 << 40),
+        (3, None, need),                              # no workspace
+        (3, A, need - 1),                             # workspace too small
+        (3, A + 4, need),                             # misaligned workspace
+    ]
+    for n_split, ws, nbytes in bad:
+        assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 1, n_split, ws, nbytes, A, None,
+                  None) == _lib.VELOX_ERR_INVALID
+        assert de(A, A, A, 1, ldq, ldkv, H, N, M, d, s, n_split, ws, nbytes, A, None,
+                  None) == _lib.VELOX_ERR_INVALID
+    assert "workspace" in lib.velox_last_error().decode() or "n_split" in lib.velox_last_error().decode()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
