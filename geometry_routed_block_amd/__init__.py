@@ -30,7 +30,7 @@ from ._lib import VELOX_BLOCK, VeloxError
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
            "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
            "gilbert_curve", "kv_append", "route_scores_shared", "slab_table", "multiwarp",
-           "token_points", "library_path", "split_workspace"]
+           "token_points", "library_path", "split_workspace", "check_routes"]
 
 
 def library_path() -> str:
@@ -199,6 +199,27 @@ def _attn_out(q, out, lse, want_lse):
     if lse is not None:
         _contig(lse, "lse")
     return out, lse
+
+
+def check_routes(route_ids, route_len, M: int):
+    """(number of invalid rows, smallest invalid row or -1): rows whose length
+    is outside [0, L] or whose ids are not strictly ascending in [0, M)."""
+    torch = _torch()
+    _require_cuda(route_ids, route_len)
+    _contig(route_ids, "route_ids")
+    _contig(route_len, "route_len")
+    if route_ids.dtype != torch.int32 or route_len.dtype != torch.int32:
+        raise TypeError("route_ids and route_len must be int32")
+    rows = route_len.numel()
+    L = route_ids.shape[-1]
+    if route_ids.numel() != rows * L:
+        raise ValueError("route_ids must hold route_len.numel() rows of L ids")
+    bad = torch.empty(2, dtype=torch.int32, device=route_ids.device)
+    lib = _lib.load()
+    _lib.check(lib.velox_route_check(route_ids.data_ptr(), route_len.data_ptr(), rows, M, L,
+                                     bad.data_ptr(), _stream(route_ids)))
+    n, first = (int(x) for x in bad.cpu().tolist())
+    return n, (first if n > 0 else -1)
 
 
 def split_workspace(q, n_split: int):

@@ -24,7 +24,7 @@ EXPORTS = ("velox_last_error", "velox_version", "velox_block_mean", "velox_route
            "velox_kv_append", "velox_route_scores_shared", "velox_sparse_attn_shared",
            "velox_slab_table", "velox_multiwarp_workspace_size", "velox_multiwarp",
            "velox_token_points", "velox_attn_split_workspace_size", "velox_sparse_attn_split",
-           "velox_dense_attn_split")
+           "velox_dense_attn_split", "velox_route_check")
 VELOX_ROUTE_FUSED, VELOX_ROUTE_MODEL_ONLY, VELOX_ROUTE_GEOMETRY_ONLY = 0, 1, 2
 VELOX_OBB_WORDS = 16
 VELOX_MAX_LATTICE = 16
@@ -106,6 +106,8 @@ def load() -> ctypes.CDLL:
     lib.velox_sparse_attn_split.restype = i32
     lib.velox_sparse_attn_split.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
                                             vp, vp, i32, i32, i32, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.velox_route_check.restype = i32
+    lib.velox_route_check.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.velox_dense_attn_split.restype = i32
     lib.velox_dense_attn_split.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, f32,
                                            i32, vp, ctypes.c_size_t, vp, vp, vp]

@@ -187,6 +187,16 @@ velox_status_t velox_route_select(const float* p, const float* g, const float* r
                   "velox_route_select");
 }
 
+velox_status_t velox_route_check(const int32_t* route_ids, const int32_t* route_len, int rows,
+                                 int M, int L, int32_t* bad, void* stream) {
+  REQUIRE(rows >= 0 && M >= 0 && L >= 1, "need rows >= 0, M >= 0, L >= 1 (got %d, %d, %d)", rows, M, L);
+  REQUIRE(bad, "bad must be non-NULL");
+  REQUIRE(rows == 0 || (route_ids && route_len), "route_ids and route_len must be non-NULL");
+  return launched(velox::launch_route_check(route_ids, route_len, rows, M, L, bad,
+                                            static_cast<hipStream_t>(stream)),
+                  "velox_route_check");
+}
+
 size_t velox_attn_split_workspace_size(int H, int N, int n_split) {
   if (H < 1 || N < 1 || n_split < 1) return 0;
   const size_t rows = static_cast<size_t>(n_split) * H * N * VELOX_BLOCK;

@@ -64,6 +64,8 @@ hipError_t launch_multiwarp(const float* src_depth, const float* src_cams, int K
 hipError_t launch_token_points(const int32_t* cells, const float* zq, int W, int H, const float* cam,
                                float f, float cx, float cy, int64_t n_tok, float* depth, float* pts,
                                hipStream_t stream);
+hipError_t launch_route_check(const int32_t* route_ids, const int32_t* route_len, int rows, int M,
+                              int L, int32_t* bad, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, bool bf16, int64_t ld_new_h, int H,
                             int T, int height, int width, int d, int chunk_index,
                             const int32_t* cells, void* k_cache, void* v_cache, int64_t ld_kv_h,

@@ -689,6 +689,40 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   if (t == 0) a.route_len[static_cast<int64_t>(h) * a.N + i] = min(carry_cnt, a.L);
 }
 
+// ---------------------------------------------------------------- route check
+//
+// One wave per route row: the row is valid when 0 <= len <= L and its first
+// len ids are strictly ascending and inside [0, M). bad[0] counts invalid
+// rows, bad[1] keeps the smallest invalid row index (h * N + i).
+
+__global__ __launch_bounds__(256) void route_check_init_kernel(int32_t* bad, int rows) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    bad[0] = 0;
+    bad[1] = rows;
+  }
+}
+
+__global__ __launch_bounds__(256) void route_check_kernel(const int32_t* __restrict__ ids,
+                                                          const int32_t* __restrict__ len, int rows,
+                                                          int M, int L, int32_t* bad) {
+  const int row = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (row >= rows) return;
+  const int n = len[row];
+  bool ok = n >= 0 && n <= L;
+  if (ok) {
+    const int32_t* r = ids + static_cast<int64_t>(row) * L;
+    for (int j = lane; j < n; j += kWave) {
+      const int id = r[j];
+      if (id < 0 || id >= M || (j > 0 && r[j - 1] >= id)) ok = false;
+    }
+  }
+  if (__ballot(!ok) != 0 && lane == 0) {
+    atomicAdd(&bad[0], 1);
+    atomicMin(&bad[1], row);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static int next_pow2(int x) {
@@ -820,6 +854,17 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3(N, H), dim3(kSelectThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_check(const int32_t* route_ids, const int32_t* route_len, int rows, int M,
+                              int L, int32_t* bad, hipStream_t stream) {
+  hipLaunchKernelGGL(route_check_init_kernel, dim3(1), dim3(64), 0, stream, bad, rows);
+  if (rows > 0) {
+    const int per = 256 / kWave;
+    hipLaunchKernelGGL(route_check_kernel, dim3((rows + per - 1) / per), dim3(256), 0, stream, route_ids,
+                       route_len, rows, M, L, bad);
+  }
   return hipGetLastError();
 }
 

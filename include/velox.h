@@ -178,6 +178,21 @@ velox_status_t velox_route_select(const float* p, const float* g, const float* r
                                   int32_t* route_ids, int32_t* route_len, void* stream);
 
 /*
+ * velox_route_check — checks what the attention calls assume of a route
+ * ([digest] Method steps, step 4: a route is a set of history block ids,
+ * emitted ascending): for every row, 0 <= route_len <= L and the first
+ * route_len ids strictly ascending and in [0, M). The attention kernels do
+ * not check this (they clamp ids into range); this call is the check for
+ * routes built outside velox_route_select. Asynchronous on `stream`.
+ *   route_ids [rows][L], route_len [rows] int32 (rows = H*N, or N for shared
+ *             routes)
+ *   bad       device int32[2] (output): bad[0] = number of invalid rows,
+ *             bad[1] = smallest invalid row index, or rows when none
+ */
+velox_status_t velox_route_check(const int32_t* route_ids, const int32_t* route_len, int rows,
+                                 int M, int L, int32_t* bad, void* stream);
+
+/*
  * velox_sparse_attn — indexed block-sparse attention ([digest] Core method,
  * eq. 15; Prerequisites: skipping a tile skips both its QK^T product and its
  * K/V load). For each (h, i) and each query row a of block i:

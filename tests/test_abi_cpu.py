@@ -132,6 +132,14 @@ def test_split_attention_validation(lib):
     assert "workspace" in lib.velox_last_error().decode() or "n_split" in lib.velox_last_error().decode()
 
 
+def test_route_check_validation(lib):
+    A = 0x10000
+    assert lib.velox_route_check(A, A, 4, 10, 8, None, None) == _lib.VELOX_ERR_INVALID
+    assert lib.velox_route_check(None, A, 4, 10, 8, A, None) == _lib.VELOX_ERR_INVALID
+    assert lib.velox_route_check(A, A, 4, 10, 0, A, None) == _lib.VELOX_ERR_INVALID
+    assert lib.velox_route_check(A, A, -1, 10, 8, A, None) == _lib.VELOX_ERR_INVALID
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

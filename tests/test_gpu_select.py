@@ -72,3 +72,28 @@ def test_select_without_reservation_takes_everything():
     rho = np.zeros(N, np.float32)
     prm = RouteParams(K_cov=M, K_unc=M, theta_unc=1.0, n_prev=0)
     _check(p, g, rho, prm)
+
+
+def test_route_check_accepts_routes_and_flags_each_fault():
+    rng = np.random.default_rng(9)
+    H, N, M = 2, 6, 300
+    p = _rows("continuous", H, N, M, rng)
+    g = rng.random((N, M)).astype(np.float32) * 0.4
+    rho = np.array([0.95, 0.2, 1.0, 0.0, 0.91, 0.5], np.float32)
+    ids, lens = velox.route_select(torch.from_numpy(p).to(DEV), torch.from_numpy(g).to(DEV),
+                                   torch.from_numpy(rho).to(DEV), None,
+                                   RouteParams(K_cov=40, K_unc=60, theta_unc=0.8, n_prev=3))
+    assert velox.check_routes(ids, lens, M) == (0, -1)
+    L = ids.shape[-1]
+    faults = {3: lambda r, n: r.__setitem__(1, r[0]),            # duplicate id
+              5: lambda r, n: r.__setitem__(slice(0, 2), r[[1, 0]]),   # descending pair
+              7: lambda r, n: r.__setitem__(n - 1, M),           # id past the history
+              8: lambda r, n: r.__setitem__(0, -3)}              # negative id
+    ids_np, lens_np = ids.cpu().numpy().reshape(H * N, L), lens.cpu().numpy().reshape(H * N)
+    for row, f in faults.items():
+        assert lens_np[row] >= 2
+        f(ids_np[row], lens_np[row])
+    lens_np[10] = L + 1                                          # longer than the buffer
+    lens_np[11] = -1
+    bad, first = velox.check_routes(torch.from_numpy(ids_np).to(DEV), torch.from_numpy(lens_np).to(DEV), M)
+    assert (bad, first) == (6, 3)
