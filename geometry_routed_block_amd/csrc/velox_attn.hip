@@ -470,6 +470,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 // phases. Each team has a two-slot ring for K and one for V (16 KiB slots,
 // 128 KiB in all); the DMA for K(j+2) and V(j+1) is issued at the start of VALU
 // phase j and has three phases to land before MFMA phase j+2 / j+1 needs it.
+// The workgroups of an XCD take their (head, pair) units longest first; with
+// split rows a unit is a range of a pair's tile lists and leaves partial
+// results for split_merge_kernel.
 
 namespace pp {
 
@@ -489,7 +492,8 @@ typedef __attribute__((address_space(1))) const char gbl_char_t;
 // at row 4 n + l / 16, physical chunk l % 16. Team wave tw issues n = tw + 4 i,
 // so n & 3 = tw is constant per wave and the logical chunk each lane fetches,
 // (l % 16) ^ ((4 n + l / 16) & 15) for K or (l % 16) ^ (4 (l / 16)) for V,
-// does not depend on i: one 32-bit lane offset serves all four instructions.
+// does not depend on i: the four instructions use one 32-bit lane offset plus
+// 4 KiB per instruction.
 __device__ __forceinline__ uint32_t dma_lane_off(int tw, int lane, bool is_v) {
   const int x = lane >> 4, p = lane & 15;
   const int c = is_v ? (p ^ (x << 2)) : (p ^ ((tw << 2) | x));
