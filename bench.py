@@ -293,6 +293,29 @@ def main():
     log(f"timed {K} steps: {ms_per_step:.3f} ms/step (scores {t_scores:.3f}, select {t_select:.3f}, "
         f"sparse {t_sparse:.3f})")
 
+    # the same step captured once in a HIP graph and replayed (no host launch
+    # work per step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    gs_, ge_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gs_.record()
+    for _ in range(K):
+        graph.replay()
+    ge_.record()
+    torch.cuda.synchronize()
+    graph_ms = gs_.elapsed_time(ge_) / K
+    log(f"graph-replayed step: {graph_ms:.3f} ms")
+    del graph
+
     # dense baseline on the same tensors
     od = torch.empty_like(q)
     velox.dense_attn(q, k, v, wl.M, out=od)
@@ -474,6 +497,7 @@ def main():
         "pct_mfma_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
         "breakdown_ms": {"route_scores": round(t_scores, 4), "route_select": round(t_select, 4),
                          "sparse_attn": round(t_sparse, 4)},
+        "ms_per_step_graph_replay": round(graph_ms, 4),
         "dense_ms": round(dense_ms, 4),
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
         "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
