@@ -153,12 +153,15 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x
 // ---------------------------------------------------------------- importance
 //
 // One workgroup (512 threads) per (group of QB query blocks, head).
-//  1. query block means: 16-byte loads, all QB blocks' loads in flight, then a
-//     reduction over row groups in LDS.
+//  1. query block means: 16-byte loads of all QB blocks issued at once, summed
+//     per lane, across the row groups of a wave by lane swaps, then across
+//     waves in LDS. The first history rows of step 2 are requested before that
+//     reduction, so their latency overlaps it.
 //  2. logits: a group of D / 8 lanes shares each history row (contiguous
 //     16-byte loads of kbar[h][r], several rows in flight); each lane dots its
 //     8 dims with the QB query means held in registers and DPP adds sum the
-//     group. Logits of the QB rows stay in LDS.
+//     group. Logits of the QB rows stay in LDS; each lane keeps the running
+//     maximum of the logits it wrote.
 //  3. softmax over the history blocks of each row (all QB rows reduced
 //     together), written coalesced: exp through the hardware exp2 and one
 //     reciprocal per row (within a few float32 ulps of the correctly rounded
@@ -194,10 +197,11 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   constexpr int kCpr = D / 8;                      // 8-element chunks per token row
   constexpr int kGroups = kScoreThreads / kCpr;    // token-row groups
   constexpr int kPasses = kBlock / kGroups;
+  constexpr int kWaves = kScoreThreads / kWave;
   extern __shared__ float smem[];
   float* qbar = smem;                              // [QB][D]
-  float* red = qbar + QB * D;                      // [kGroups][D]
-  float* logit = red + kGroups * D;                // [QB][M]
+  float* red = qbar + QB * D;                      // [kWaves][QB][D] partial sums, then reductions
+  float* logit = red + kWaves * QB * D;            // [QB][M]
   // one-dimensional grid of H * groups workgroups, remapped so that the
   // groups of a head share an XCD (its kbar rows are read once into that L2)
   const int groups = (N + QB - 1) / QB;
@@ -205,59 +209,32 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   const int h = wg / groups, i0 = (wg % groups) * QB, t = threadIdx.x;
   const int nq = min(QB, N - i0);
 
-  // 1. query block means, two blocks' loads in flight at a time
-  {
-    const int c8 = t % kCpr, grp = t / kCpr;
-    for (int qb0 = 0; qb0 < nq; qb0 += 2) {
-      const int nb = min(2, nq - qb0);
-      float acc[2][8];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
-        if (b < nb) {
-          const T* src = q + h * ld_q_h + static_cast<int64_t>(i0 + qb0 + b) * kBlock * D + c8 * 8;
-#pragma unroll
-          for (int ps = 0; ps < kPasses; ++ps) {
-            float x[8];
-            load8<T>(src + (ps * kGroups + grp) * D, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[b][e] += x[e];
-          }
-        }
-      }
-      for (int b = 0; b < nb; ++b) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[grp * D + c8 * 8 + e] = b == 0 ? acc[0][e] : acc[1][e];
-        __syncthreads();
-        if (t < D) {
-          float s = 0.f;
-          for (int g2 = 0; g2 < kGroups; ++g2) s += red[g2 * D + t];
-          qbar[(qb0 + b) * D + t] = s * (1.0f / kBlock);
-        }
-        __syncthreads();
-      }
-    }
-  }
-
-  // 2. logits. The lanes of a group of kLpr = D / 8 lanes share one history
-  // row: lane j8 loads its 8 dims (a row is read contiguously by its group)
-  // and dots them with the same 8 dims of every query mean, which it keeps in
-  // registers; DPP adds then sum the group's partials (every lane ends with
-  // the row's dot products). The loads of the next kBatch rows are issued
-  // before the arithmetic of the current ones.
+  // 1. query block means. Blocks past the group's last re-read the last block
+  // (no branch around the loads); their sums are not stored.
   constexpr int kLpr = D / 8, kRpw = kWave / kLpr;
   constexpr int kRowsPerIt = kRpw * (kScoreThreads / kWave);
   const int lane = t % kWave, wv = t / kWave;
   const int j8 = lane % kLpr, rg = lane / kLpr;
-  float qv[QB][8];
+  float acc[QB][8];
+  {
+    const int c8 = t % kCpr, grp = t / kCpr;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int b = 0; b < QB; ++b) {
+      const T* src = q + h * ld_q_h + static_cast<int64_t>(min(i0 + b, N - 1)) * kBlock * D + c8 * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + j8 * 8 + e] : 0.f;
+      for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        float x[8];
+        load8<T>(src + (ps * kGroups + grp) * D, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] += x[e];
+      }
+    }
+  }
+  // first history rows of step 2 (rows past the end load the last row; their
+  // dot products are not stored)
   const float* kb = kbar + h * ld_kbar_h;
-  // rows past the end load the last row (no branch around the loads, so the
-  // compiler can count them); their dot products are not stored
   auto load_row = [&](int r, float (&x)[8]) {
     const float4* src =
         reinterpret_cast<const float4*>(kb + static_cast<int64_t>(min(r, M - 1)) * D + j8 * 8);
@@ -272,6 +249,53 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) load_row(r_me + b * kRowsPerIt, kx[b]);
   }
+  {
+    // the lanes of a wave holding the same chunk (lane mod kCpr) differ in
+    // bits 3 (D = 64), 4 and 5: swap-and-add over those bits, ascending
+    const int c8 = t % kCpr;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[b][e];
+        if constexpr (kCpr == 8) {
+          const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false);  // row_ror:8
+          v += __int_as_float(y);
+        }
+        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+        acc[b][e] = v;
+      }
+    if (lane < kCpr) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[(wv * QB + b) * D + c8 * 8 + e] = acc[b][e];
+    }
+    __syncthreads();
+    for (int x = t; x < nq * D; x += kScoreThreads) {
+      const int b = x / D, d = x % D;
+      float sum = 0.f;
+      for (int w2 = 0; w2 < kWaves; ++w2) sum += red[(w2 * QB + b) * D + d];
+      qbar[x] = sum * (1.0f / kBlock);
+    }
+    __syncthreads();
+  }
+
+  // 2. logits. The lanes of a group of kLpr = D / 8 lanes share one history
+  // row: lane j8 loads its 8 dims (a row is read contiguously by its group)
+  // and dots them with the same 8 dims of every query mean, which it keeps in
+  // registers; DPP adds then sum the group's partials (every lane ends with
+  // the row's dot products). The loads of the next kBatch rows are issued
+  // before the arithmetic of the current ones.
+  float qv[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + j8 * 8 + e] : 0.f;
+  float lmax = -INFINITY;  // running maximum of the logits this lane stores
   for (int r0 = 0; r0 < M; r0 += kBatch * kRowsPerIt) {
     float nx[kBatch][8];
 #pragma unroll
@@ -288,7 +312,10 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
         acc = group_sum<kLpr>(acc);
         if (j8 == qb) mine = acc;
       }
-      if (r < M && j8 < nq) logit[j8 * M + r] = mine * scale;
+      if (r < M && j8 < nq) {
+        logit[j8 * M + r] = mine * scale;
+        lmax = fmaxf(lmax, mine * scale);
+      }
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b)
@@ -305,24 +332,28 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     return;
   }
 
-  // 3. softmax over the history blocks of each row, all rows at once: maxima,
-  // then exponentials and sums, then the normalised values written coalesced
-  // (`red` is free again and holds the per-wave partials)
-  constexpr int kWaves = kScoreThreads / kWave;
+  // 3. softmax over the history blocks of each row, all rows at once: maxima
+  // (lanes j8 of every wave hold partial maxima of row j8), then exponentials
+  // and sums, then the normalised values written coalesced (`red` is free
+  // again and holds the per-wave partials)
+  {
+    float v = lmax;
+    if constexpr (kRpw == 8) {
+      const int y = __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x128, 0xf, 0xf, false);
+      v = fmaxf(v, __int_as_float(y));
+    }
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+    if (lane < kLpr) red[wv * kLpr + lane] = v;
+  }
+  __syncthreads();
   float mx[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mx[qb] = -INFINITY;
-    if (qb < nq)
-      for (int r = t; r < M; r += kScoreThreads) mx[qb] = fmaxf(mx[qb], logit[qb * M + r]);
-    mx[qb] = wave_max(mx[qb]);
-    if (lane == 0) red[qb * kWaves + wv] = mx[qb];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float m = red[qb * kWaves];
-    for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, red[qb * kWaves + w2]);
+    float m = red[qb];
+    for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, red[w2 * kLpr + qb]);
     mx[qb] = m;
   }
   __syncthreads();
@@ -744,8 +775,8 @@ hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, in
 }
 
 size_t route_scores_lds_bytes(int qb, int M, int d) {
-  const int groups = kScoreThreads / (d / 8);
-  return sizeof(float) * (static_cast<size_t>(qb) * d + static_cast<size_t>(groups) * d +
+  const int waves = kScoreThreads / kWave;
+  return sizeof(float) * (static_cast<size_t>(qb) * d + static_cast<size_t>(waves) * qb * d +
                           static_cast<size_t>(qb) * M);
 }
 
