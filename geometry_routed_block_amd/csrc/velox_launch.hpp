@@ -45,7 +45,7 @@ hipError_t launch_route_scores(const void* q, bool bf16, int64_t ld_q_h, const f
 hipError_t launch_route_scores_shared(const void* q, bool bf16, int64_t ld_q_h, const float* kbar,
                                       int64_t ld_kbar_h, int H, int N, int M, int d, float scale,
                                       float* logits, float* p, hipStream_t stream);
-size_t route_select_lds_bytes(int M);
+size_t route_select_lds_bytes(int M, int fs);
 hipError_t launch_route_select(const float* p, const float* g, const float* rho,
                                const int32_t* coord, int H, int N, int M, const RouteConfig& cfg,
                                int L, int32_t* route_ids, int32_t* route_len, hipStream_t stream);

@@ -417,7 +417,8 @@ __global__ __launch_bounds__(kScoreThreads) void head_mean_softmax_kernel(
 
 // ---------------------------------------------------------------- route select
 //
-// One workgroup (512 threads) per (query block, head).
+// One workgroup (256 threads) per (query block, head); LDS is sized by the
+// largest cap of the call, so that all rows of a call fit on the GPU at once.
 //  1. fused weight w (fp32, one rounding per operation), fixed-point mass W,
 //     total Z and reserved mass; sort key = (~bits(w) << 32) | id so that
 //     ascending key order ranks by w descending, then id ascending (w >= 0);
@@ -440,6 +441,7 @@ struct SelectArgs {
   int32_t* route_ids;
   int32_t* route_len;
   int N, M, L, P2, nwords;
+  int fs;  // capacity of the selected-key buffers: the largest radix-select cap
   float tau, g_ref, lambda, eta_cov, theta_cov, theta_unc;
   int K_cov, K_unc, n_prev, neigh26, n_ref, mode;
 };
@@ -449,7 +451,7 @@ struct SelectArgs {
 //   1 model only:     w = p                            (same budgets, no geometry)
 //   2 geometry only:  w = g, top-K_cov, no mass cut    (hard geometric top-K)
 
-constexpr int kSelectThreads = 512;
+constexpr int kSelectThreads = 256;
 constexpr int kFastSel = 1024;   // largest cap served by the radix select
 
 // Control words of the radix select, in LDS.
@@ -477,7 +479,7 @@ __device__ __forceinline__ bool mass_reached(uint64_t m, uint64_t thq, uint64_t 
 
 __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs a) {
   extern __shared__ uint64_t sel_smem[];
-  const int fs = min(a.P2, kFastSel);
+  const int fs = a.fs;
   uint64_t* keys = sel_smem;                                      // [P2]
   uint64_t* sel = keys + a.P2;                                    // [fs]
   uint64_t* ordered = sel + fs;                                   // [fs]
@@ -498,28 +500,65 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
 
   for (int wd = t; wd < a.nwords; wd += nt) mask[wd] = 0u;
 
-  // 1. weights, masses, keys
+  // 1. weights, masses, keys. The loads of kChunk rows per thread are issued
+  // before their arithmetic (rows past the end re-read the last row). The
+  // 26-neighbour test of the same rows is kept in `nbits` (bit k: the k-th row
+  // of this thread) and entered in the mask after the barrier below, when the
+  // clear above has completed; threads with more than 32 rows test later.
+  constexpr int kChunk = 4;
+  const bool nb_early = a.neigh26 && a.P2 <= 32 * nt;
+  int qt = 0, qh = 0, qw = 0;
+  if (a.neigh26) {
+    const int32_t* qc = a.coord + 3 * static_cast<int64_t>(M + i);
+    qt = qc[0];
+    qh = qc[1];
+    qw = qc[2];
+  }
   uint64_t zloc = 0, mloc = 0;
-  for (int r = t; r < a.P2; r += nt) {
-    uint64_t key = ~0ull;
-    if (r < M) {
-      float w = prow[r];
-      if (covered && a.mode == 0) {
-        const float g = grow[r];
-        const float gh = (g > a.tau) ? fminf(__fdiv_rn(g, a.g_ref), 1.0f) : 0.0f;
-        const float u = __fadd_rn(1.0f, __fmul_rn(a.lambda, gh));
-        w = __fmul_rn(w, u);
-      } else if (covered && a.mode == 2) {
-        w = grow[r];
+  uint32_t nbits = 0;
+  for (int r0 = t, k0 = 0; r0 < a.P2; r0 += kChunk * nt, k0 += kChunk) {
+    float pw[kChunk], gw[kChunk];
+    int cd[kChunk];  // Chebyshev distance of the row's block to the query block
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      pw[u] = 0.f;
+      gw[u] = 0.f;
+      cd[u] = 0;
+      if (M > 0) {
+        const int rr = min(r0 + u * nt, M - 1);
+        pw[u] = prow[rr];
+        gw[u] = grow[rr];
+        if (nb_early) {
+          const int32_t* rc = a.coord + 3 * static_cast<int64_t>(rr);
+          cd[u] = max(abs(rc[0] - qt), max(abs(rc[1] - qh), abs(rc[2] - qw)));
+        }
       }
-      const uint64_t W = fixed_mass(w);
-      zloc += W;
-      if (r >= res0)
-        mloc += W;
-      else
-        key = (static_cast<uint64_t>(~__float_as_uint(w)) << 32) | static_cast<uint32_t>(r);
     }
-    keys[r] = key;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int r = r0 + u * nt;
+      if (r >= a.P2) break;
+      uint64_t key = ~0ull;
+      if (r < M) {
+        float w = pw[u];
+        if (covered && a.mode == 0) {
+          const float g = gw[u];
+          const float gh = (g > a.tau) ? fminf(__fdiv_rn(g, a.g_ref), 1.0f) : 0.0f;
+          const float uu = __fadd_rn(1.0f, __fmul_rn(a.lambda, gh));
+          w = __fmul_rn(w, uu);
+        } else if (covered && a.mode == 2) {
+          w = gw[u];
+        }
+        const uint64_t W = fixed_mass(w);
+        zloc += W;
+        if (r >= res0)
+          mloc += W;
+        else
+          key = (static_cast<uint64_t>(~__float_as_uint(w)) << 32) | static_cast<uint32_t>(r);
+        if (nb_early && cd[u] == 1) nbits |= 1u << (k0 + u);
+      }
+      keys[r] = key;
+    }
   }
   zloc = wave_sum_u64(zloc);
   mloc = wave_sum_u64(mloc);
@@ -532,6 +571,12 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   for (int j = 0; j < nwv; ++j) {
     Z += red64[j];
     m0 += red64[8 + j];
+  }
+  while (nbits) {
+    const int k = __ffs(nbits) - 1;
+    nbits &= nbits - 1;
+    const int r = t + k * nt;
+    atomicOr(&mask[r >> 5], 1u << (r & 31));
   }
 
   // caps of this row
@@ -670,9 +715,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     const uint32_t r = static_cast<uint32_t>(top[j]);
     atomicOr(&mask[r >> 5], 1u << (r & 31));
   }
-  if (a.neigh26) {
-    const int32_t* qc = a.coord + 3 * static_cast<int64_t>(M + i);
-    const int qt = qc[0], qh = qc[1], qw = qc[2];
+  if (a.neigh26 && !nb_early) {
     for (int r = t; r < M; r += nt) {
       const int32_t* rc = a.coord + 3 * static_cast<int64_t>(r);
       const int dist = max(abs(rc[0] - qt), max(abs(rc[1] - qh), abs(rc[2] - qw)));
@@ -685,13 +728,15 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   }
   __syncthreads();
 
-  // 5. ascending emission: exclusive scan of per-word popcounts
+  // 5. ascending emission: exclusive prefix of the words' popcounts (in the
+  // key buffer, free now), then route slot s takes the s-th set bit: the word
+  // by binary search over the prefixes, the bit by halving the word.
   int32_t* out = a.route_ids + (static_cast<int64_t>(h) * a.N + i) * a.L;
+  int* wpre = reinterpret_cast<int*>(keys);  // [nwords]
   int carry_cnt = 0;
   for (int base = 0; base < a.nwords; base += nt) {
     const int wd = base + t;
-    const uint32_t bits = wd < a.nwords ? mask[wd] : 0u;
-    const int cnt = __popc(bits);
+    const int cnt = wd < a.nwords ? __popc(mask[wd]) : 0;
     int incl = cnt;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -705,18 +750,33 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
       if (w2 < wv) before += wscan[w2];
       total += wscan[w2];
     }
-    int pos = carry_cnt + before + incl - cnt;
-    uint32_t b = bits;
-    while (b) {
-      const int bit = __ffs(b) - 1;
-      b &= b - 1;
-      if (pos < a.L) out[pos] = wd * 32 + bit;
-      ++pos;
-    }
+    if (wd < a.nwords) wpre[wd] = carry_cnt + before + incl - cnt;
     carry_cnt += total;
     __syncthreads();
   }
-  for (int s = carry_cnt + t; s < a.L; s += nt) out[s] = -1;
+  for (int sl = t; sl < a.L; sl += nt) {
+    int id = -1;
+    if (sl < carry_cnt) {
+      int lo = 0, hi = a.nwords - 1;  // last word whose prefix is <= sl
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (wpre[mid] <= sl) lo = mid; else hi = mid - 1;
+      }
+      uint32_t bits = mask[lo];
+      int k = sl - wpre[lo], bit = 0;  // k-th set bit of bits
+#pragma unroll
+      for (int width = 16; width > 0; width >>= 1) {
+        const int c = __popc(bits & ((1u << width) - 1u));
+        if (k >= c) {
+          k -= c;
+          bits >>= width;
+          bit += width;
+        }
+      }
+      id = lo * 32 + bit;
+    }
+    out[sl] = id;
+  }
   if (t == 0) a.route_len[static_cast<int64_t>(h) * a.N + i] = min(carry_cnt, a.L);
 }
 
@@ -842,9 +902,18 @@ hipError_t launch_route_scores_shared(const void* q, bool bf16, int64_t ld_q_h, 
   return hipGetLastError();
 }
 
-size_t route_select_lds_bytes(int M) {
+// Largest number of keys a row of the call gathers by radix select: the cap
+// beyond the reservation, at most M - reserved and kFastSel (larger caps sort).
+static int select_capacity(int M, const RouteConfig& cfg) {
+  const int n_res = cfg.n_prev < M ? cfg.n_prev : M;
+  int cap = cfg.K_cov > cfg.K_unc ? cfg.K_cov : cfg.K_unc;
+  cap = cap - n_res < M - n_res ? cap - n_res : M - n_res;
+  if (cap > kFastSel) cap = kFastSel;
+  return cap > 1 ? cap : 1;
+}
+
+size_t route_select_lds_bytes(int M, int fs) {
   const int P2 = next_pow2(M > 0 ? M : 1);
-  const int fs = P2 < kFastSel ? P2 : kFastSel;
   const int nwords = (M + 31) / 32;
   return sizeof(uint64_t) * (P2 + 2 * fs + 16) + sizeof(SelectCtl) + sizeof(int) * 256 +
          sizeof(uint32_t) * nwords + sizeof(int) * 16;
@@ -867,6 +936,7 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
   a.L = L;
   a.P2 = next_pow2(M > 0 ? M : 1);
   a.nwords = (M + 31) / 32;
+  a.fs = select_capacity(M, cfg);
   a.tau = cfg.tau;
   a.g_ref = cfg.g_ref;
   a.lambda = cfg.lambda;
@@ -879,7 +949,7 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
   a.neigh26 = cfg.neigh26;
   a.n_ref = cfg.n_ref;
   a.mode = cfg.mode;
-  const size_t lds = route_select_lds_bytes(M);
+  const size_t lds = route_select_lds_bytes(M, a.fs);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));

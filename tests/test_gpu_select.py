@@ -1,7 +1,9 @@
 """GPU parity of route materialisation on crafted importances: exact ties
 (routes decided by block index alone), zero weights, caps that take every
-candidate, and caps above the radix-select limit (the sort fallback). Routes
-are compared bit for bit with the oracle."""
+candidate, caps above the radix-select limit (the sort fallback), and
+26-neighbour safeguards on a history long enough that the kernel tests the
+neighbours in its late loop. Routes are compared bit for bit with the
+oracle."""
 
 import numpy as np
 import pytest
@@ -97,3 +99,22 @@ def test_route_check_accepts_routes_and_flags_each_fault():
     lens_np[11] = -1
     bad, first = velox.check_routes(torch.from_numpy(ids_np).to(DEV), torch.from_numpy(lens_np).to(DEV), M)
     assert (bad, first) == (6, 3)
+
+
+def test_select_neighbours_on_a_long_history():
+    # 9000 history blocks (a 30 x 15 x 20 block grid, frame-major) and query
+    # blocks one frame later: more than 32 candidate rows per thread, where the
+    # kernel fills the neighbour bits in its late loop instead of during the
+    # weight pass
+    rng = np.random.default_rng(21)
+    H, N, T, Y, X = 1, 4, 30, 15, 20
+    M = T * Y * X
+    hist = np.stack(np.meshgrid(np.arange(T), np.arange(Y), np.arange(X), indexing="ij"), -1).reshape(-1, 3)
+    query = np.array([[T, 0, 0], [T, 7, 9], [T, 14, 19], [T + 1, 3, 3]])   # corner, middle, corner, two frames on
+    coords = np.ascontiguousarray(np.concatenate([hist, query]).astype(np.int32))
+    say(f"select with neighbours, M={M}")
+    p = _rows("continuous", H, N, M, rng)
+    g = rng.random((N, M)).astype(np.float32) * 0.4
+    rho = np.array([0.95, 0.2, 1.0, 0.5], np.float32)
+    prm = RouteParams(K_cov=60, K_unc=90, theta_unc=0.7, n_prev=X, neigh26=1)   # reserves one grid row
+    _check(p, g, rho, prm, coords)
