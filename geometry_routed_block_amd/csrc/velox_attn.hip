@@ -578,10 +578,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       for (int e = t; e < nr; e += kThreads)
         lens_s[e] = min(max(a.route_len[route_row(a, h_lo + e / N, e % N)], 0), a.L);
       __syncthreads();
+      // rank of each row among its head's rows, and of each unit below among
+      // the XCD's units: eight LDS reads in flight per wait
+      auto rank_of = [](const int* vals, int lo, int hi, int me, int vme) {
+        int rank = 0, o = lo;
+        for (; o + 8 <= hi; o += 8) {
+          int x[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = vals[o + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) rank += (x[u] > vme) || (x[u] == vme && o + u < me);
+        }
+        for (; o < hi; ++o) rank += (vals[o] > vme) || (vals[o] == vme && o < me);
+        return rank;
+      };
       for (int e = t; e < nr; e += kThreads) {
         const int hb = e - e % N, lr = lens_s[e];
-        int rank = 0;
-        for (int o = hb; o < hb + N; ++o) rank += (lens_s[o] > lr) || (lens_s[o] == lr && o < e);
+        const int rank = rank_of(lens_s, hb, hb + N, e, lr);
         rank_s[e] = rank;
         sorted_s[hb + rank] = lr;
       }
@@ -592,9 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       }
       __syncthreads();
       for (int w = t; w < cnt; w += kThreads) {
-        const int cw = cost_s[w];
-        int rank = 0;
-        for (int v = 0; v < cnt; ++v) rank += (cost_s[v] > cw) || (cost_s[v] == cw && v < w);
+        const int rank = rank_of(cost_s, 0, cnt, w, cost_s[w]);
         if (rank == slot) pair_rows[0] = base + w;  // the one pair of dispatch rank `slot`
       }
       __syncthreads();
