@@ -132,3 +132,22 @@ def test_kv_append_places_every_token_once_and_means_its_blocks():
     assert np.allclose(kbar[:, 2], placed[:, :128].astype(np.float64).mean(1))
     assert np.allclose(kbar[:, 3], placed[:, 128:].astype(np.float64).mean(1))
     assert (kbar[:, [0, 1, 4]] == 0).all()
+
+
+@pytest.mark.parametrize("T,H,W", [(3, 3, 4), (3, 32, 48), (1, 29, 52), (2, 4, 9)])
+def test_chunk_parity_of_the_flip(T, H, W):
+    # [project] "Keeping neighbours adjacent in the block order", Figure 7
+    # caption: chunk 0 keeps the single-chunk curve and chunk 1 is the one
+    # flipped horizontally (alternate chunks). The curve starts at cell (0, 0)
+    # (pinned above against the textbook Hilbert curve and the path test), so
+    # the first token of chunk 0 is frame 0 at column 0 and the first token of
+    # chunk 1 is frame 0 at the last column; chunk 2 repeats chunk 0.
+    for chunk in range(4):
+        pos = _positions(T, H, W, chunk)
+        assert pos[0] == (T * chunk, 0, 0 if chunk % 2 == 0 else W - 1)
+        rank = layout.cell_rank_map(H, W)
+        ranks = layout.chunk_token_ranks(T, H, W, chunk)
+        for h in range(H):
+            for w in range(W):
+                wq = w if chunk % 2 == 0 else W - 1 - w
+                assert ranks[h * W + w] == rank[h, wq] * T

@@ -170,6 +170,14 @@ def test_route_worked_examples():
         assert got == case["expect"], case["why"]
 
 
+def test_route_mass_threshold_reached_exactly():
+    gd = _load("route_threshold_exact.json")
+    for case in gd["cases"]:
+        kw = {k: case[k] for k in ("K_cov", "K_unc", "theta_cov", "theta_unc", "n_prev") if k in case}
+        got = _route_case(gd["p"], gd["g"], case["rho"], RouteParams(**kw), 3)
+        assert got == case["expect"], case["why"]
+
+
 def _rank_key(w, r):
     return (-Fraction(float(w[r])), r)
 

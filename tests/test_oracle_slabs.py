@@ -161,3 +161,53 @@ def test_higher_resolution_source_fills_every_cell():
     zq2, chosen2 = slabs.multiwarp([D], [c], 4 * W, 4 * H, (4 * f, 2 * W, 2 * H), c, W, H, (f, W / 2, H / 2),
                                    k_warp=17)
     assert (chosen2 == -1).all() and np.isnan(zq2).all()
+
+
+def test_token_points_closed_form_on_a_fronto_parallel_plane():
+    # Camera at c = (1, 2, 3) looking down +z (R = I), pinhole f = 2,
+    # (cx, cy) = (2, 1.5) on a 4 x 3 token grid; every cell at depth 4. A token
+    # in cell (col, row) is lifted through the cell centre (col + 1/2, row + 1/2):
+    #   X = 1 + 4 (col + 1/2 - 2) / 2,  Y = 2 + 4 (1.5 - row - 1/2) / 2,  Z = 3 + 4,
+    # all exact in float32. Cells outside the grid take the nearest edge cell;
+    # a cell without depth (NaN) or with depth <= 0 gives a NaN point.
+    W, H, f, cx, cy = 4, 3, 2.0, 2.0, 1.5
+    zq = np.full(W * H, 4.0, f32)
+    zq[1 * W + 2] = np.nan        # cell (col 2, row 1)
+    zq[2 * W + 3] = 0.0           # cell (col 3, row 2): unreliable
+    cells = np.array([[0, 0], [3, 0], [1, 2], [2, 1], [3, 2], [-5, 1], [9, 7]], np.int32)
+    depth, pts = slabs.token_points(cells, zq, W, H, cam(np.eye(3), (1.0, 2.0, 3.0)), f, cx, cy)
+
+    def expect(col, row):
+        return [1 + 4 * (col + 0.5 - cx) / f, 2 + 4 * (cy - row - 0.5) / f, 7.0]
+    assert pts[0].tolist() == expect(0, 0) == [-2.0, 4.0, 7.0]
+    assert pts[1].tolist() == expect(3, 0)
+    assert pts[2].tolist() == expect(1, 2)
+    assert np.isnan(pts[3]).all() and np.isnan(depth[3])
+    assert np.isnan(pts[4]).all() and depth[4] == 0.0
+    assert pts[5].tolist() == expect(0, 1) and depth[5] == 4.0     # clamped to column 0
+    assert np.isnan(pts[6]).all()                                   # clamped onto (3, 2): depth 0
+
+
+def test_slab_table_uses_each_blocks_own_camera():
+    # [onedev] "How it works" / [digest] Method steps, step 1: a block's slab is
+    # its token rectangle in the latent camera of the chunk it came from. Two
+    # blocks with the same samples but different cameras: each box centre must
+    # project back onto its rectangle centre at mid-depth in its own camera,
+    # and not in the other block's camera.
+    cams = np.stack([cam(rot([0.0, 1.0, 0.2], 0.4), (0.5, 0.0, -1.0)),
+                     cam(rot([1.0, 0.3, 0.0], -0.6), (-2.0, 1.0, 0.5))])
+    rng = np.random.default_rng(3)
+    cols = rng.integers(10, 20, 128)
+    rows = rng.integers(5, 12, 128)
+    z = rng.uniform(2.0, 6.0, 128).astype(f32)
+    cells = np.concatenate([np.stack([cols, rows], 1)] * 2)
+    depth = np.concatenate([z, z])
+    sl, boxes = slabs.slab_table(cells, depth, cams, np.array([0, 1]), F, CX, CY, 8)
+    assert (sl[0] == sl[1]).all()
+    for b, other in ((0, 1), (1, 0)):
+        u0, u1, v0, v1, zlo, zhi = (float(x) for x in sl[b][:6])
+        uc, vc, zm = (u0 + u1) / 2, (v0 + v1) / 2, (zlo + zhi) / 2
+        pu, pv, pz = slabs.project(cams[b], boxes[b][0:3], F, CX, CY)
+        assert abs(pu - uc) < 1e-4 and abs(pv - vc) < 1e-4 and abs(pz - zm) < 1e-5
+        qu, qv, _ = slabs.project(cams[other], boxes[b][0:3], F, CX, CY)
+        assert abs(qu - uc) + abs(qv - vc) > 1.0
