@@ -138,21 +138,30 @@ def route_scores_shared(q, kbar, M: int, scale: float | None = None, logits=None
     return out
 
 
-def route_bound(params, M: int) -> int:
-    """Smallest route length L that always suffices."""
+def route_bound(params, M: int, n_ref: int | None = None) -> int:
+    """Smallest route length L that always suffices (n_ref: number of
+    reference ids, default len(params.ref_ids))."""
     kmax = max(int(params.K_cov), int(params.K_unc), int(params.n_prev))
-    bound = kmax + 26 * int(params.neigh26) + len(tuple(params.ref_ids))
+    n_ref = len(tuple(params.ref_ids)) if n_ref is None else int(n_ref)
+    bound = kmax + 26 * int(params.neigh26) + n_ref
     return max(1, min(M, bound))
 
 
 def route_select(p, g, rho, coord, params, L: int | None = None, route_ids=None,
-                 route_len=None):
+                 route_len=None, ref_ids=None, status=None):
     """Routes (route_ids [H][N][L] int32, route_len [H][N] int32).
 
     `params` is any object with the attributes tau, g_ref, lam, eta_cov,
     theta_cov, theta_unc, K_cov, K_unc, n_prev, neigh26 and ref_ids (a sequence
     of history ids), and optionally mode (0 fused, 1 model only, 2 geometry
     only; default 0).
+    ref_ids: optional int32 device tensor of reference-frame ids; when given it
+    replaces params.ref_ids and nothing is allocated or copied per call (the
+    form a captured HIP graph needs). Without it, a non-empty params.ref_ids is
+    copied to the device on every call.
+    status: optional int32 device tensor of 2 elements that receives the
+    input report (rows whose p or g break the fixed-point preconditions, and
+    the smallest such row h * N + i, or H * N).
     """
     torch = _torch()
     _require_cuda(p, g, rho)
@@ -161,23 +170,52 @@ def route_select(p, g, rho, coord, params, L: int | None = None, route_ids=None,
         _contig(t, name)
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
+    if tuple(g.shape) != (N, M) or rho.numel() != N:
+        raise ValueError(f"g must be [N][M] = [{N}][{M}] and rho [N] (got {tuple(g.shape)}, "
+                         f"{tuple(rho.shape)})")
     if coord is not None:
         _require_cuda(coord)
         _contig(coord, "coord")
         if coord.dtype != torch.int32:
             raise TypeError("coord must be int32")
-    L = route_bound(params, M) if L is None else L
+        if coord.numel() < 3 * (M + N) or coord.numel() % 3:
+            raise ValueError(f"coord must be [>=M+N][3] = [>={M + N}][3] (got {tuple(coord.shape)})")
+    L = route_bound(params, M, None if ref_ids is None else ref_ids.numel()) if L is None else L
     if route_ids is None:
         route_ids = torch.empty(H, N, L, dtype=torch.int32, device=p.device)
     if route_len is None:
         route_len = torch.empty(H, N, dtype=torch.int32, device=p.device)
-    ref = tuple(int(r) for r in params.ref_ids)
-    ref_t = torch.tensor(ref, dtype=torch.int32, device=p.device) if ref else None
+    _require_cuda(route_ids, route_len)
+    _contig(route_ids, "route_ids")
+    _contig(route_len, "route_len")
+    if route_ids.dtype != torch.int32 or route_len.dtype != torch.int32:
+        raise TypeError("route_ids and route_len must be int32")
+    if route_ids.numel() != H * N * L or route_len.numel() != H * N:
+        raise ValueError(f"route_ids must be [H][N][L] = [{H}][{N}][{L}] and route_len [H][N]")
+    ref_t = None
+    if ref_ids is not None:
+        _require_cuda(ref_ids)
+        _contig(ref_ids, "ref_ids")
+        if ref_ids.dtype != torch.int32:
+            raise TypeError("ref_ids must be int32")
+        n_ref = ref_ids.numel()
+        ref_ptr = ref_ids.data_ptr() if n_ref else None
+    else:
+        ref = tuple(int(r) for r in params.ref_ids)
+        ref_t = torch.tensor(ref, dtype=torch.int32, device=p.device) if ref else None
+        n_ref = len(ref)
+        ref_ptr = ref_t.data_ptr() if ref_t is not None else None
+    st_ptr = None
+    if status is not None:
+        _require_cuda(status)
+        _contig(status, "status")
+        if status.dtype != torch.int32 or status.numel() < 2:
+            raise ValueError("status must be an int32 device tensor of 2 elements")
+        st_ptr = status.data_ptr()
     c = _lib.RouteParamsC(params.tau, params.g_ref, params.lam, params.eta_cov, params.theta_cov,
                           params.theta_unc, int(params.K_cov), int(params.K_unc),
-                          int(params.n_prev), int(params.neigh26),
-                          ref_t.data_ptr() if ref_t is not None else None, len(ref),
-                          int(getattr(params, "mode", 0)))
+                          int(params.n_prev), int(params.neigh26), ref_ptr, n_ref,
+                          int(getattr(params, "mode", 0)), st_ptr)
     lib = _lib.load()
     _lib.check(lib.velox_route_select(p.data_ptr(), g.data_ptr(), rho.data_ptr(),
                                       coord.data_ptr() if coord is not None else None, H, N, M,
@@ -193,12 +231,26 @@ def _attn_out(q, out, lse, want_lse):
     H, NT, d = q.shape
     if out is None:
         out = torch.empty(H, NT, d, dtype=q.dtype, device=q.device)
+    _require_cuda(out)
     _contig(out, "out")
+    if out.dtype != q.dtype or out.numel() != H * NT * d:
+        raise ValueError(f"out must be [H][N*128][d] = [{H}][{NT}][{d}] of q's dtype")
     if lse is None and want_lse:
         lse = torch.empty(H, NT, dtype=torch.float32, device=q.device)
     if lse is not None:
+        _require_cuda(lse)
         _contig(lse, "lse")
+        if lse.dtype != torch.float32 or lse.numel() != H * NT:
+            raise ValueError(f"lse must be float32 [H][N*128] = [{H}][{NT}]")
     return out, lse
+
+
+def _kv_rows(q, k, v, M):
+    """k and v must hold the M history blocks and the N current ones."""
+    H, NT, d = q.shape
+    if k.shape[0] != H or k.shape[2] != d or k.shape[1] < M * VELOX_BLOCK + NT:
+        raise ValueError(f"k and v must be [H][>=(M+N)*128][d] = [{H}][>={M * VELOX_BLOCK + NT}][{d}] "
+                         f"(got {tuple(k.shape)})")
 
 
 def check_routes(route_ids, route_len, M: int):
@@ -257,6 +309,9 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
         raise ValueError("q, k, v must share a dtype and k, v a layout")
     _contig(route_ids, "route_ids")
     _contig(route_len, "route_len")
+    if route_ids.dtype != _torch().int32 or route_len.dtype != _torch().int32:
+        raise TypeError("route_ids and route_len must be int32")
+    _kv_rows(q, k, v, M)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
     lib = _lib.load()
@@ -290,6 +345,7 @@ def dense_attn(q, k, v, M: int, scale: float | None = None, out=None, lse=None,
     N = NT // VELOX_BLOCK
     if k.dtype != q.dtype or v.dtype != q.dtype or k.stride() != v.stride():
         raise ValueError("q, k, v must share a dtype and k, v a layout")
+    _kv_rows(q, k, v, M)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
     lib = _lib.load()

@@ -38,7 +38,7 @@ class RouteParamsC(ctypes.Structure):
         ("eta_cov", ctypes.c_float), ("theta_cov", ctypes.c_float), ("theta_unc", ctypes.c_float),
         ("K_cov", ctypes.c_int32), ("K_unc", ctypes.c_int32), ("n_prev", ctypes.c_int32),
         ("neigh26", ctypes.c_int32), ("ref_ids", ctypes.c_void_p), ("n_ref", ctypes.c_int32),
-        ("mode", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("status", ctypes.c_void_p),
     ]
 
 

@@ -181,7 +181,7 @@ velox_status_t velox_route_select(const float* p, const float* g, const float* r
   velox::RouteConfig cfg{prm->tau,       prm->g_ref,     prm->lambda, prm->eta_cov,
                          prm->theta_cov, prm->theta_unc, prm->K_cov,  prm->K_unc,
                          prm->n_prev,    prm->neigh26,   prm->mode,   prm->ref_ids,
-                         prm->n_ref};
+                         prm->n_ref,     prm->status};
   return launched(velox::launch_route_select(p, g, rho, coord, H, N, M, cfg, L, route_ids, route_len,
                                              static_cast<hipStream_t>(stream)),
                   "velox_route_select");

@@ -14,6 +14,7 @@ struct RouteConfig {
   int K_cov, K_unc, n_prev, neigh26, mode;
   const int32_t* ref_ids;
   int n_ref;
+  int32_t* status;  // nullable device int32[2]: rows with bad inputs, smallest such row
 };
 
 struct AttnConfig {

@@ -431,6 +431,12 @@ __global__ __launch_bounds__(kScoreThreads) void head_mean_softmax_kernel(
 //  3. count c of taken candidates: the cap, or the first prefix whose mass
 //     meets the threshold (block-wide scan of the ordered masses).
 //  4. route = reserved ∪ first c ∪ safeguards as an LDS bitmask; emit ascending.
+// Inputs outside what the fixed-point mass allows are reported per row in the
+// optional status word: an entry of p that is negative, NaN or infinite, an
+// entry of g outside [0, 1] (NaN included), or, on a row with a mass cut, a
+// total sum_r floor(w_r 2^60) that does not fit in 64 bits (impossible when the
+// row's p sums to at most 1 + 2^-10 and lambda <= 14). Such a row still gets
+// an in-range ascending route, computed from saturated masses.
 
 struct SelectArgs {
   const float* p;
@@ -440,6 +446,7 @@ struct SelectArgs {
   const int32_t* ref_ids;
   int32_t* route_ids;
   int32_t* route_len;
+  int32_t* status;  // nullable: [0] rows with bad inputs, [1] smallest such row
   int N, M, L, P2, nwords;
   int fs;  // capacity of the selected-key buffers: the largest radix-select cap
   float tau, g_ref, lambda, eta_cov, theta_cov, theta_unc;
@@ -483,8 +490,8 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   uint64_t* keys = sel_smem;                                      // [P2]
   uint64_t* sel = keys + a.P2;                                    // [fs]
   uint64_t* ordered = sel + fs;                                   // [fs]
-  uint64_t* red64 = ordered + fs;                                 // [2 * 8 waves]
-  SelectCtl* ctl = reinterpret_cast<SelectCtl*>(red64 + 16);
+  uint64_t* red64 = ordered + fs;                                 // [3 * 8 waves + 1]
+  SelectCtl* ctl = reinterpret_cast<SelectCtl*>(red64 + 25);
   int* hist = reinterpret_cast<int*>(ctl + 1);                    // [256]
   uint32_t* mask = reinterpret_cast<uint32_t*>(hist + 256);       // [nwords]
   int* wscan = reinterpret_cast<int*>(mask + a.nwords);           // [8 waves + 2]
@@ -514,7 +521,10 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     qh = qc[1];
     qw = qc[2];
   }
-  uint64_t zloc = 0, mloc = 0;
+  // Z is summed as high and low 32-bit halves of each W (neither sum can
+  // overflow for M <= 2^16), so that a total of 2^64 or more is detected.
+  uint64_t zhi = 0, zlo = 0, mloc = 0;
+  bool bad_in = false, big = false;
   uint32_t nbits = 0;
   for (int r0 = t, k0 = 0; r0 < a.P2; r0 += kChunk * nt, k0 += kChunk) {
     float pw[kChunk], gw[kChunk];
@@ -541,6 +551,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
       uint64_t key = ~0ull;
       if (r < M) {
         float w = pw[u];
+        bad_in |= !(w >= 0.f && w <= 3.402823466e38f) || !(gw[u] >= 0.f && gw[u] <= 1.f);
         if (covered && a.mode == 0) {
           const float g = gw[u];
           const float gh = (g > a.tau) ? fminf(__fdiv_rn(g, a.g_ref), 1.0f) : 0.0f;
@@ -549,8 +560,11 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
         } else if (covered && a.mode == 2) {
           w = gw[u];
         }
-        const uint64_t W = fixed_mass(w);
-        zloc += W;
+        const bool fits = w < 16.f;  // else w 2^60 >= 2^64 (NaN fails too)
+        big |= !fits;
+        const uint64_t W = fits ? fixed_mass(w) : ~0ull;
+        zhi += W >> 32;
+        zlo += W & 0xffffffffull;
         if (r >= res0)
           mloc += W;
         else
@@ -560,18 +574,30 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
       keys[r] = key;
     }
   }
-  zloc = wave_sum_u64(zloc);
+  zhi = wave_sum_u64(zhi);
+  zlo = wave_sum_u64(zlo);
   mloc = wave_sum_u64(mloc);
+  const bool wave_bad = __ballot(bad_in) != 0, wave_big = __ballot(big) != 0;
+  if (t == 0) red64[24] = 0;
+  __syncthreads();
   if (lane == 0) {
-    red64[wv] = zloc;
+    red64[wv] = zhi;
     red64[8 + wv] = mloc;
+    red64[16 + wv] = zlo;
+    if (wave_bad || wave_big)
+      atomicOr(reinterpret_cast<unsigned long long*>(&red64[24]),
+               (wave_bad ? 1ull : 0ull) | (wave_big ? 2ull : 0ull));
   }
   __syncthreads();
-  uint64_t Z = 0, m0 = 0;
+  uint64_t zh = 0, zl = 0, m0 = 0;
   for (int j = 0; j < nwv; ++j) {
-    Z += red64[j];
+    zh += red64[j];
     m0 += red64[8 + j];
+    zl += red64[16 + j];
   }
+  const uint64_t Z = (zh << 32) + zl;  // modulo 2^64
+  const bool z_overflow = (red64[24] & 2ull) != 0 || zh + (zl >> 32) >= (1ull << 32);
+  const bool input_bad = (red64[24] & 1ull) != 0;
   while (nbits) {
     const int k = __ffs(nbits) - 1;
     nbits &= nbits - 1;
@@ -585,6 +611,10 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   const float theta = covered ? (a.mode == 2 ? 1.0f : a.theta_cov) : a.theta_unc;
   const int limit = max(0, min(K - n_res, M - n_res));
   const bool cut = theta < 1.0f && limit > 0;
+  if (a.status && t == 0 && (input_bad || (cut && z_overflow))) {
+    atomicAdd(&a.status[0], 1);
+    atomicMin(&a.status[1], h * a.N + i);
+  }
 
   // 2. the `limit` smallest keys, in `top` (ascending when cut)
   const uint64_t* top = keys;
@@ -685,7 +715,8 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     uint64_t carry = m0;
     for (int base = 0; base < limit; base += nt) {
       const int j = base + t;
-      const uint64_t Wj = j < limit ? fixed_mass(key_weight(top[j])) : 0ull;
+      const float wj = j < limit ? key_weight(top[j]) : 0.f;
+      const uint64_t Wj = wj < 16.f ? fixed_mass(wj) : ~0ull;
       // inclusive scan of Wj over the workgroup
       uint64_t incl = Wj;
 #pragma unroll
@@ -915,7 +946,7 @@ static int select_capacity(int M, const RouteConfig& cfg) {
 size_t route_select_lds_bytes(int M, int fs) {
   const int P2 = next_pow2(M > 0 ? M : 1);
   const int nwords = (M + 31) / 32;
-  return sizeof(uint64_t) * (P2 + 2 * fs + 16) + sizeof(SelectCtl) + sizeof(int) * 256 +
+  return sizeof(uint64_t) * (P2 + 2 * fs + 25) + sizeof(SelectCtl) + sizeof(int) * 256 +
          sizeof(uint32_t) * nwords + sizeof(int) * 16;
 }
 
@@ -949,6 +980,12 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
   a.neigh26 = cfg.neigh26;
   a.n_ref = cfg.n_ref;
   a.mode = cfg.mode;
+  a.status = cfg.status;
+  if (a.status) {
+    hipLaunchKernelGGL(route_check_init_kernel, dim3(1), dim3(64), 0, stream, a.status, H * N);
+    const hipError_t ei = hipGetLastError();
+    if (ei != hipSuccess) return ei;
+  }
   const size_t lds = route_select_lds_bytes(M, a.fs);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -84,6 +84,9 @@ typedef struct {
                        (1, w = p with the same budgets: the matched model-only
                        block-sparse route), VELOX_ROUTE_GEOMETRY_ONLY (2, w = g,
                        plain top-K_cov with no mass cut: hard geometric top-K) */
+  int32_t* status;  /* DEVICE int32[2] or NULL: input report of velox_route_select
+                       (see there); status[0] = rows with bad inputs, status[1] =
+                       the smallest such row h*N + i, or H*N when there is none */
 } velox_route_params_t;
 
 #define VELOX_ROUTE_FUSED 0
@@ -169,8 +172,15 @@ velox_status_t velox_route_scores_shared(const void* q, velox_dtype_t dt, int64_
  *   route_len [H][N] int32 (output)
  * L must be >= min(M, max(K_cov, K_unc, n_prev) + 26*neigh26 + n_ref) and >= 1.
  * (With duplicated cells a row could exceed this; it is then cut to its L
- * smallest ids.) p rows must be non-negative with sum <= 1 + 2^-10; g must be
- * in [0, 1].
+ * smallest ids.)
+ * Input preconditions, checked on the device per row: every p entry finite and
+ * >= 0, every g entry in [0, 1], and, on a row with a mass cut (theta < 1),
+ * a fixed-point total Z < 2^64 (guaranteed when the row of p sums to at most
+ * 1 + 2^-10, since lambda <= 14). A row that breaks one is counted in
+ * prm->status when that pointer is non-NULL (the call clears it first, with a
+ * launch of its own); its route is still ascending, unique and in [0, M), but
+ * computed from saturated masses, so it carries no meaning. The call itself
+ * returns VELOX_OK: the check runs asynchronously on the device.
  */
 velox_status_t velox_route_select(const float* p, const float* g, const float* rho,
                                   const int32_t* coord, int H, int N, int M,

@@ -68,49 +68,27 @@ def test_wan13_full_path():
     check_attention_rows(wl, qn, kn, vn, o_d, lse_d, None, sample_rows(wl, 6, 6), dense=True)
 
 
-def test_chunk48_full_size_sampled():
-    """Full chunk-48 shape (the benchmarked launch): all 1440 routes exact, p on
-    sampled heads, attention on sampled rows, dense on a few rows."""
-    wl = synth.chunk48()
-    say("chunk48: generating inputs on the GPU")
-    q, k, v = synth.make_qkv(wl, device=DEV)
-    r = run_path(wl, q, k, v)
-    say("chunk48: routes")
-    routes = check_routes_exact(wl, r["p"], r["ids"], r["lens"])
-    heads = [0, 17, 39]
-    qn = to_np(q[heads])
-    kn = to_np(k[heads])
-    vn = to_np(v[heads])
-    say("chunk48: importance")
-    for j, h in enumerate(heads):
-        qb = oracle.block_means(qn[j:j + 1])
-        kb = oracle.block_means(kn[j:j + 1, : wl.M * 128])
-        np.testing.assert_allclose(r["kbar"][h].cpu().numpy(), kb[0], rtol=1e-5, atol=1e-6)
-        np.testing.assert_allclose(r["p"][h].cpu().numpy(), oracle.importance(qb, kb, wl.scale)[0],
-                                   rtol=P_RTOL, atol=1e-30)
-    say("chunk48: attention rows")
-    sub = synth.Workload(**{**wl.__dict__, "H": len(heads)})
-    sub_routes = [routes[h] for h in heads]
-    rows = [(0, 0), (0, 35), (1, 7), (1, 20), (2, 3), (2, 30)]
-    o_sub = r["o"][heads]
-    lse_sub = r["lse"][heads]
-    check_attention_rows(sub, qn, kn, vn, o_sub, lse_sub, sub_routes, rows)
-    say("chunk48: dense rows")
-    o_d, lse_d = velox.dense_attn(q, k, v, wl.M, want_lse=True)
-    check_attention_rows(sub, qn, kn, vn, o_d[heads], lse_d[heads], None, [(0, 1), (2, 34)],
-                         dense=True)
-
-
-@pytest.mark.parametrize("frac", [0.0, 1.0])
-def test_chunk48_coverage_sweep_routes(frac):
+@pytest.mark.parametrize("frac", [0.0, 0.5, 1.0])
+def test_chunk48_coverage_sweep(frac):
+    """Coverage sweep at the chunk-48 shape: every route bit-exact, and
+    attention on sampled rows of covered and uncovered blocks."""
     wl = synth.sweep(frac)
     say(f"sweep coverage {frac}")
     q, k, v = synth.make_qkv(wl, device=DEV)
     r = run_path(wl, q, k, v)
-    check_routes_exact(wl, r["p"], r["ids"], r["lens"])
+    routes = check_routes_exact(wl, r["p"], r["ids"], r["lens"])
     lens = r["lens"].cpu().numpy()
-    K = wl.params.K_cov if frac == 1.0 else wl.params.K_unc
-    assert lens.max() <= K and lens.min() >= wl.params.n_prev
+    cov = wl.rho >= np.float32(wl.params.eta_cov)
+    assert cov.mean() == pytest.approx(frac, abs=1 / wl.N)
+    assert (lens[:, cov] <= wl.params.K_cov).all() and (lens[:, ~cov] <= wl.params.K_unc).all()
+    assert lens.min() >= wl.params.n_prev
+    rows = sample_rows(wl, 10, 40 + int(frac * 10))
+    heads = sorted({h for h, _ in rows})
+    sub = synth.Workload(**{**wl.__dict__, "H": len(heads)})
+    qn, kn, vn = to_np(q[heads]), to_np(k[heads]), to_np(v[heads])
+    sub_rows = [(heads.index(h), i) for h, i in rows]
+    check_attention_rows(sub, qn, kn, vn, r["o"][heads], r["lse"][heads],
+                         [routes[h] for h in heads], sub_rows)
 
 
 def test_sparse_with_every_tile_equals_dense_bitwise():
