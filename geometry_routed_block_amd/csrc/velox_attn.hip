@@ -692,19 +692,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
 
   const int qrow = (i >= 0 ? i : 0) * kBlock + tw * 32 + l32;  // this lane's query row
   const bf16_t* qh = static_cast<const bf16_t*>(a.q) + h * a.ld_q_h;
+  // Q fragments, pre-multiplied by scale * log2(e) and rounded to bf16
+  // (round to nearest even), so that S = K Q^T comes out in the exp2 domain.
+  const float sc = a.scale * 1.4426950408889634f;
   bf16x8_t qf[8];
 #pragma unroll
-  for (int ds = 0; ds < 8; ++ds)
-    qf[ds] = __builtin_bit_cast(
+  for (int ds = 0; ds < 8; ++ds) {
+    const bf16x8_t raw = __builtin_bit_cast(
         bf16x8_t, *reinterpret_cast<const u32x4_t*>(qh + static_cast<int64_t>(qrow) * D + ds * 16 + hh * 8));
+    qf[ds] = __builtin_convertvector(__builtin_convertvector(raw, f32x8_t) * sc, bf16x8_t);
+  }
 
   f32x16_t o_acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o_acc[db] = f32x16_t{};
   f32x16_t s_acc[2];
   bf16x8_t pf[4];
-  float m_ref = -INFINITY, l_run = 0.f;
-  const float sc = a.scale * 1.4426950408889634f;
+  // m_ref: this lane's query's reference max (exp2 domain); neg_m holds -m_ref
+  // in all 16 accumulator slots and is the C operand of the first QK^T MFMA,
+  // so each score reaches the softmax as x = s - m_ref.
+  float m_ref = 0.f, l_run = 0.f;
+  f32x16_t neg_m = f32x16_t{};
 
   // K fragment (row kb*32 + l32, logical chunk 2 ds + hh) sits at byte
   //   kb*8192 + l32*256 + 16 (hh ^ z0) + 32 (ds ^ z1),  z = l32 & 15.
@@ -788,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (u + kAhead < 16) fb[u + kAhead] = load_k(ksl, (u + kAhead) & 1, (u + kAhead) >> 1);
       const int kb = u & 1, ds = u >> 1;
-      s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u], qf[ds], ds == 0 ? f32x16_t{} : s_acc[kb], 0, 0, 0);
+      s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u], qf[ds], ds == 0 ? neg_m : s_acc[kb], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -814,43 +822,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     const uint64_t hk = half_off(j + 2, id_next);
     if (v_next) dma_half(vg + hoff_next, m0v[decltype(Q)::value], voff);
     hoff_next = hk;
-    // softmax of S(j) against the lazy reference max
-    float m0 = s_acc[0][0], m1 = s_acc[1][0];
+    // softmax of S(j): p = 2^x with x = s - m_ref straight from the MFMA. The
+    // reference moves lazily: on the first half-tile of the range, and when
+    // the half-tile's sum of p exceeds 32 * 2^8 (some x above 13; a row of 32
+    // values all <= 8 sums to at most that), a wave-uniform slow path takes
+    // the query's true maximum x_max (both halves of the row) and, when it is
+    // above 8 (always on the first half-tile), moves m_ref up by x_max,
+    // rescales O and l by 2^-x_max and recomputes p. Otherwise p <= 2^13.
+    f32x8_t e[4];
+    auto exps = [&](float shift) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      m0 = fmaxf(m0, s_acc[0][r]);
-      m1 = fmaxf(m1, s_acc[1][r]);
-    }
-    float mx = fmaxf(m0, m1);
-    {  // lanes l and l ^ 32 hold the same query: exchange halves without LDS
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
-    }
-    if (__ballot(mx > m_ref + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
-    }
-    float ps[4];
+        for (int r = 0; r < 8; ++r) {
+          e[2 * kb][r] = __builtin_amdgcn_exp2f(s_acc[kb][r] - shift);
+          e[2 * kb + 1][r] = __builtin_amdgcn_exp2f(s_acc[kb][8 + r] - shift);
+        }
+    };
+    auto row_sum = [&] {  // pairwise tree over the 32 values
+      f32x8_t t = (e[0] + e[1]) + (e[2] + e[3]);
+      const float a0 = (t[0] + t[1]) + (t[2] + t[3]);
+      const float a1 = (t[4] + t[5]) + (t[6] + t[7]);
+      return a0 + a1;
+    };
+    exps(0.f);
+    float ps = row_sum();
+    if (__ballot(j == 0 || !(ps <= 8192.0f)) != 0) {
+      float m0 = fmaxf(fmaxf(s_acc[0][0], s_acc[0][1]), fmaxf(s_acc[1][0], s_acc[1][1]));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x8_t lo, hi;
-      ps[2 * kb] = 0.f;
-      ps[2 * kb + 1] = 0.f;
+      for (int r = 2; r < 16; r += 2)
+        m0 = fmaxf(m0, fmaxf(fmaxf(s_acc[0][r], s_acc[0][r + 1]), fmaxf(s_acc[1][r], s_acc[1][r + 1])));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m0), false, false);
+      const float xmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float shift = (j == 0 || xmax > kLazyRescale) ? xmax : 0.f;
+      if (j != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        l_run *= alpha;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        lo[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][r], sc, -m_ref));
-        hi[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][8 + r], sc, -m_ref));
-        ps[2 * kb] += lo[r];
-        ps[2 * kb + 1] += hi[r];
+        for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
       }
-      pf[2 * kb] = __builtin_convertvector(lo, bf16x8_t);
-      pf[2 * kb + 1] = __builtin_convertvector(hi, bf16x8_t);
+      m_ref += shift;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) neg_m[r] = -m_ref;
+      exps(shift);
+      ps = row_sum();
     }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) pf[q4] = __builtin_convertvector(e[q4], bf16x8_t);
+    l_run += ps;
     __builtin_amdgcn_sched_barrier(0);
     if (k_next) dma_half(kg + hk, m0k[decltype(P)::value], koff);
     // K(j+1) and V(j), issued one VALU phase ago, must have landed before the
