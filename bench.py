@@ -252,6 +252,7 @@ def main():
     ids = torch.empty(wl.H, wl.N, L, dtype=torch.int32, device=dev)
     lens = torch.empty(wl.H, wl.N, dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
+    ws = velox.attn_workspace(q, L)
     torch.cuda.synchronize()
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -265,7 +266,7 @@ def main():
     def step():
         velox.route_scores(q, kbar, wl.M, out=p)
         velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
-        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o)
+        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -284,7 +285,7 @@ def main():
         e[1].record()
         velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
         e[2].record()
-        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o)
+        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o, workspace=ws)
         e[3].record()
     end.record()
     torch.cuda.synchronize()

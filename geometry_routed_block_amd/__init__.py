@@ -30,7 +30,7 @@ from ._lib import VELOX_BLOCK, VeloxError
 __all__ = ["VELOX_BLOCK", "VeloxError", "block_mean", "route_scores", "route_select",
            "route_bound", "sparse_attn", "dense_attn", "slab_overlap", "slab_coverage",
            "gilbert_curve", "kv_append", "route_scores_shared", "slab_table", "multiwarp",
-           "token_points", "library_path", "split_workspace", "check_routes"]
+           "token_points", "library_path", "split_workspace", "attn_workspace", "check_routes"]
 
 
 def library_path() -> str:
@@ -274,6 +274,14 @@ def check_routes(route_ids, route_len, M: int):
     return n, (first if n > 0 else -1)
 
 
+def attn_workspace(q, L: int):
+    """A device workspace for sparse_attn (its unit schedule; uint8 tensor)."""
+    torch = _torch()
+    H, NT, d = q.shape
+    nbytes = _lib.load().velox_sparse_attn_workspace_size(H, NT // VELOX_BLOCK, int(L), d)
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=q.device)
+
+
 def split_workspace(q, n_split: int):
     """A device workspace for the split-row attention calls (uint8 tensor)."""
     torch = _torch()
@@ -300,7 +308,9 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
     (or [1][N][L] / [1][N]) one route per query block shared by all heads.
     n_split > 1 cuts every row's tiles into that many ranges (per-head routes
     only); `workspace` is then a device buffer of split_workspace(q, n_split)'s
-    size (allocated here when None).
+    size (allocated here when None). With per-head routes and n_split = 1 the
+    workspace holds the call's unit schedule: attn_workspace(q, L) bytes
+    (allocated here when None).
     """
     _require_cuda(q, k, v, route_ids, route_len)
     H, NT, d = q.shape
@@ -328,11 +338,20 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
             route_ids.shape[-1], 1 if include_current else 0, int(n_split), ws.data_ptr(), ws_bytes,
             out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q)))
         return (out, lse) if want_lse or lse is not None else out
-    fn = lib.velox_sparse_attn_shared if shared else lib.velox_sparse_attn
-    _lib.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), _rows(q, "q"),
-                  _rows(k, "k"), H, N, M, d, ctypes.c_float(scale), route_ids.data_ptr(),
-                  route_len.data_ptr(), route_ids.shape[-1], 1 if include_current else 0,
-                  out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q)))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), _rows(q, "q"),
+            _rows(k, "k"), H, N, M, d, ctypes.c_float(scale), route_ids.data_ptr(),
+            route_len.data_ptr(), route_ids.shape[-1], 1 if include_current else 0,
+            out.data_ptr(), lse.data_ptr() if lse is not None else None)
+    if shared:
+        _lib.check(lib.velox_sparse_attn_shared(*args, _stream(q)))
+    else:
+        if workspace is None:
+            workspace = attn_workspace(q, route_ids.shape[-1])
+        _require_cuda(workspace)
+        need = lib.velox_sparse_attn_workspace_size(H, N, route_ids.shape[-1], d)
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace must hold {need} bytes")
+        _lib.check(lib.velox_sparse_attn(*args, workspace.data_ptr(), _stream(q)))
     return (out, lse) if want_lse or lse is not None else out
 
 

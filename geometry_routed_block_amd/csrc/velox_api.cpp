@@ -200,11 +200,16 @@ velox_status_t velox_route_check(const int32_t* route_ids, const int32_t* route_
 size_t velox_attn_split_workspace_size(int H, int N, int n_split) {
   if (H < 1 || N < 1 || n_split < 1) return 0;
   const size_t rows = static_cast<size_t>(n_split) * H * N * VELOX_BLOCK;
-  return rows * (128 + 2) * sizeof(float);
+  return rows * (128 + 2) * sizeof(float) + velox::attn_plan_bytes(H, N, n_split);
+}
+
+size_t velox_sparse_attn_workspace_size(int H, int N, int L, int d) {
+  if (L < 1 || d < 1) return 0;
+  return velox::attn_plan_bytes(H, N, 1);
 }
 
 // Split settings into the launch config: the workspace holds part_o
-// [n_split][rows][128] then part_ml [n_split][rows][2].
+// [n_split][rows][128], then part_ml [n_split][rows][2], then the unit plan.
 static velox_status_t set_split(velox::AttnConfig& c, int n_split, void* workspace,
                                 size_t workspace_bytes) {
   REQUIRE(n_split >= 1 && n_split <= VELOX_MAX_SPLIT, "n_split must be in [1, %d] (got %d)",
@@ -216,8 +221,10 @@ static velox_status_t set_split(velox::AttnConfig& c, int n_split, void* workspa
   REQUIRE(workspace_bytes >= need, "workspace of %zu bytes is smaller than the %zu needed",
           workspace_bytes, need);
   REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 16 == 0, "workspace must be 16-byte aligned");
+  const size_t rows = static_cast<size_t>(n_split) * c.H * c.N * VELOX_BLOCK;
   c.part_o = static_cast<float*>(workspace);
-  c.part_ml = c.part_o + static_cast<size_t>(n_split) * c.H * c.N * VELOX_BLOCK * 128;
+  c.part_ml = c.part_o + rows * 128;
+  if (c.route_ids) c.plan = c.part_ml + rows * 2;
   return VELOX_OK;
 }
 
@@ -226,14 +233,17 @@ static velox_status_t sparse_common(const void* q, const void* k, const void* v,
                                     float scale, const int32_t* route_ids, const int32_t* route_len,
                                     int L, int include_current, void* o, float* lse, void* stream,
                                     bool shared, const char* what, int n_split = 1,
-                                    void* workspace = nullptr, size_t workspace_bytes = 0) {
+                                    void* workspace = nullptr, size_t workspace_bytes = 0,
+                                    void* plan = nullptr) {
   velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
   if (st != VELOX_OK) return st;
   REQUIRE(route_ids && route_len, "route_ids and route_len must be non-NULL");
   REQUIRE(L >= 1, "L must be >= 1");
   REQUIRE(include_current == 0 || include_current == 1, "include_current must be 0 or 1");
+  REQUIRE(reinterpret_cast<uintptr_t>(plan) % 16 == 0, "workspace must be 16-byte aligned");
   velox::AttnConfig c{q, k, v, dt == VELOX_BF16, ld_q_h, ld_kv_h, H, N, M, d, scale,
                       route_ids, route_len, L, shared, include_current, o, lse};
+  c.plan = plan;
   st = set_split(c, n_split, workspace, workspace_bytes);
   if (st != VELOX_OK) return st;
   return launched(velox::launch_attention(c, static_cast<hipStream_t>(stream)), what);
@@ -242,9 +252,11 @@ static velox_status_t sparse_common(const void* q, const void* k, const void* v,
 velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v, velox_dtype_t dt,
                                  int64_t ld_q_h, int64_t ld_kv_h, int H, int N, int M, int d,
                                  float scale, const int32_t* route_ids, const int32_t* route_len,
-                                 int L, int include_current, void* o, float* lse, void* stream) {
+                                 int L, int include_current, void* o, float* lse, void* workspace,
+                                 void* stream) {
   return sparse_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, route_ids, route_len, L,
-                       include_current, o, lse, stream, false, "velox_sparse_attn");
+                       include_current, o, lse, stream, false, "velox_sparse_attn", 1, nullptr, 0,
+                       workspace);
 }
 
 velox_status_t velox_sparse_attn_shared(const void* q, const void* k, const void* v,

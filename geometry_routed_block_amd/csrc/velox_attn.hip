@@ -66,6 +66,10 @@ struct AttnArgs {
   int n_split;
   float* part_o;
   float* part_ml;
+  // Unit schedule of the routed d = 128 bf16 kernel written by plan_kernel
+  // (nullptr: every workgroup ranks the units itself): entry b is the unit of
+  // workgroup b, {head, longer row, shorter row or -1, range}.
+  const int4* plan;
 };
 
 // Route row of (head h, query block i).
@@ -565,7 +569,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   int* lens_s = &route_lds[0][0];
   int h, pr, split;
   if (t < 2) pair_rows[t] = -1;
-  if (kRouted) {
+  if (kRouted && a.plan) {
+    const int4 u = a.plan[blockIdx.x];
+    h = u.x;
+    split = u.w;
+    pr = 0;
+    __syncthreads();
+    if (t < 2) pair_rows[t] = t == 0 ? u.y : u.z;
+  } else if (kRouted) {
     const int x = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
     int base, cnt;
     xcd_range(x, G, base, cnt);
@@ -801,7 +812,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
   // P: parity of j (Even / Odd), Q: the other parity
+  // The wave in its MFMA phase gets the higher issue priority, so that the
+  // softmax of the other team's wave on the same SIMD fills the gaps between
+  // MFMA issues instead of delaying them.
   auto mfma_phase = [&](int j, auto P, auto Q) {
+    __builtin_amdgcn_s_setprio(2);
     const int rid = route_raw(j + 2);
     if (j > 0) pv_stream(vslot(Q));             // O += P(j-1) V(j-1)
     if (j < S) qk_stream(kslot(P) + kbase);     // S(j) = K(j) Q^T
@@ -818,6 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     // refill the slots MFMA(j) just freed: V(j+1) into V(j-1)'s now, K(j+2)
     // into K(j)'s after the softmax (both orders are correct; this one measured
     // 1-2% faster than issuing both first)
+    __builtin_amdgcn_s_setprio(0);
     const bool k_next = j + 2 < S, v_next = j + 1 < S;
     const uint64_t hk = half_off(j + 2, id_next);
     if (v_next) dma_half(vg + hoff_next, m0v[decltype(Q)::value], voff);
@@ -964,6 +980,98 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     a.lse[static_cast<int64_t>(h) * N * kBlock + qrow] = m_ref * 0.6931471805599453f + logf(l_tot);
 }
 
+
+// ---------------------------------------------------------------- unit schedule
+//
+// plan_kernel writes the schedule of the routed kernel once per call, so that
+// no attention workgroup spends its start ranking units. One workgroup per
+// XCD: its contiguous range of (head, pair, range) ids (xcd_range), where a
+// pair is ranks 2 pr and 2 pr + 1 of the head's rows ordered by route length
+// (longest first, ties by row), and a unit's cost is its longer row's tile
+// count. The units are ordered by cost, longest first (ties by id), and unit
+// of dispatch rank `slot` on XCD x goes to workgroup slot * 8 + x; the
+// hardware dispatches workgroups in id order as CUs free up, which makes the
+// launch a longest-processing-time list schedule on every XCD. When the rows
+// of an XCD do not fit in LDS, the units keep their id order (ranks are then
+// counted in global memory).
+struct PlanArgs {
+  const int32_t* route_len;
+  int route_head_rows;
+  int H, N, M, L, include_current, n_split;
+  int4* plan;
+};
+
+constexpr int kPlanThreads = 512;
+constexpr int kPlanLdsInts = 12288;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int sh[kPlanLdsInts];
+  const int t = threadIdx.x, x = blockIdx.x;
+  const int N = a.N, pairs = (N + 1) / 2, nsp = max(a.n_split, 1);
+  const int G = a.H * pairs * nsp;
+  int base, cnt;
+  xcd_range(x, G, base, cnt);
+  if (cnt <= 0) return;
+  const int h_lo = base / nsp / pairs, nh = (base + cnt - 1) / nsp / pairs - h_lo + 1;
+  const int nr = nh * N;
+  const int ncur = a.include_current ? N : 0;
+  auto row_len = [&](int h, int r) {
+    return a.M == 0 ? 0 : min(max(a.route_len[static_cast<int64_t>(h) * a.route_head_rows + r], 0), a.L);
+  };
+  // the row of rank `rank` in head h, by a scan of the head's lengths
+  auto rank_in_head = [](const int* lens, int n, int me, int vme) {
+    int rank = 0;
+    for (int o = 0; o < n; ++o) rank += (lens[o] > vme) || (lens[o] == vme && o < me);
+    return rank;
+  };
+  if (3 * nr + cnt <= kPlanLdsInts) {
+    int* lens_s = sh;              // [nr]
+    int* row_of = lens_s + nr;     // [nr]: row of rank k in its head
+    int* cost_s = row_of + nr;     // [cnt]
+    int* rank_s = cost_s + cnt;    // [nr]
+    for (int e = t; e < nr; e += kPlanThreads) lens_s[e] = row_len(h_lo + e / N, e % N);
+    __syncthreads();
+    for (int e = t; e < nr; e += kPlanThreads) {
+      const int hb = e - e % N;
+      const int rank = rank_in_head(lens_s + hb, N, e - hb, lens_s[e]);
+      rank_s[e] = rank;
+      row_of[hb + rank] = e - hb;
+    }
+    __syncthreads();
+    for (int w = t; w < cnt; w += kPlanThreads) {
+      const int id = (base + w) / nsp;
+      cost_s[w] = lens_s[(id / pairs - h_lo) * N + row_of[(id / pairs - h_lo) * N + 2 * (id % pairs)]] + ncur;
+    }
+    __syncthreads();
+    for (int w = t; w < cnt; w += kPlanThreads) {
+      const int cw = cost_s[w];
+      int slot = 0;
+      for (int o = 0; o < cnt; ++o) slot += (cost_s[o] > cw) || (cost_s[o] == cw && o < w);
+      const int id = base + w, hp = id / nsp, h = hp / pairs, pr = hp % pairs;
+      const int hb = (h - h_lo) * N;
+      const int ra = row_of[hb + 2 * pr];
+      const int rb = 2 * pr + 1 < N ? row_of[hb + 2 * pr + 1] : -1;
+      a.plan[slot * kXcd + x] = make_int4(h, ra, rb, id % nsp);
+    }
+  } else {
+    for (int w = t; w < cnt; w += kPlanThreads) {
+      const int id = base + w, hp = id / nsp, h = hp / pairs, pr = hp % pairs;
+      int ra = -1, rb = -1;
+      for (int r = 0; r < N; ++r) {
+        const int lr = row_len(h, r);
+        int rank = 0;
+        for (int o = 0; o < N; ++o) {
+          const int lo = row_len(h, o);
+          rank += (lo > lr) || (lo == lr && o < r);
+        }
+        if (rank == 2 * pr) ra = r;
+        if (rank == 2 * pr + 1) rb = r;
+      }
+      a.plan[w * kXcd + x] = make_int4(h, ra, rb, id % nsp);
+    }
+  }
+}
+
 }  // namespace pp
 
 // Combines the n_split ranges of every query row (four threads per row, 32
@@ -1090,8 +1198,17 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
   if (bf16 && D == 128 && (!kRouted || args.L <= pp::kMaxRoute)) {
     const int pairs = (args.N + 1) / 2;
     const int nsp = args.n_split > 1 ? args.n_split : 1;
+    AttnArgs run = args;
+    if (!kRouted) run.plan = nullptr;
+    if (kRouted && run.plan) {
+      pp::PlanArgs pa{args.route_len, args.route_head_rows, args.G / args.N, args.N, args.M,
+                      args.L, args.include_current, nsp, const_cast<int4*>(run.plan)};
+      hipLaunchKernelGGL(pp::plan_kernel, dim3(kXcd), dim3(pp::kPlanThreads), 0, stream, pa);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((pp::attn_kernel<kRouted>), dim3((args.G / args.N) * pairs * nsp),
-                       dim3(pp::kThreads), 0, stream, args);
+                       dim3(pp::kThreads), 0, stream, run);
     if (nsp > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1111,6 +1228,12 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
   else
     hipLaunchKernelGGL((attn_f32_kernel<D, kRouted>), dim3(args.G), dim3(256), 0, stream, args);
   return hipGetLastError();
+}
+
+size_t attn_plan_bytes(int H, int N, int n_split) {
+  if (H < 1 || N < 1) return 0;
+  const size_t units = static_cast<size_t>(H) * ((N + 1) / 2) * (n_split > 1 ? n_split : 1);
+  return units * sizeof(int4);
 }
 
 hipError_t launch_attention(const AttnConfig& c, hipStream_t stream) {
@@ -1137,6 +1260,7 @@ hipError_t launch_attention(const AttnConfig& c, hipStream_t stream) {
   a.n_split = pp_path && c.n_split > 1 ? c.n_split : 1;
   a.part_o = c.part_o;
   a.part_ml = c.part_ml;
+  a.plan = pp_path && routed ? static_cast<const int4*>(c.plan) : nullptr;
   if (c.d == 128)
     return routed ? launch_one<128, true>(a, c.bf16, stream) : launch_one<128, false>(a, c.bf16, stream);
   return routed ? launch_one<64, true>(a, c.bf16, stream) : launch_one<64, false>(a, c.bf16, stream);

@@ -35,7 +35,12 @@ struct AttnConfig {
   int n_split;               // > 1: split rows (d = 128 bf16 only), with the two buffers below
   float* part_o;             // [n_split][H][N*128][128] fp32
   float* part_ml;            // [n_split][H][N*128][2] fp32
+  void* plan;                // nullable: unit schedule of the routed d = 128 bf16 kernel,
+                             // attn_plan_bytes(H, N, n_split) bytes, 16-byte aligned
 };
+
+// Bytes of the unit schedule of a routed call (0 when the call needs none).
+size_t attn_plan_bytes(int H, int N, int n_split);
 
 hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, int nblk, int d,
                              float* xbar, int64_t ld_bar_h, hipStream_t stream);

@@ -219,12 +219,25 @@ velox_status_t velox_route_check(const int32_t* route_ids, const int32_t* route_
  *   lse      [H][N*128] fp32 natural-log sum of exp of the scaled logits
  *            (output, may be NULL)
  * A row with no tile at all gets o = 0 and lse = -inf.
+ *   workspace  device buffer of at least velox_sparse_attn_workspace_size(H, N,
+ *              L, d) bytes, 16-byte aligned, caller-owned, contents undefined
+ *              on return; the call writes its unit schedule there (which pairs
+ *              of rows share a workgroup and in which order the workgroups take
+ *              them: rows of a head ranked by route length, each XCD's units
+ *              longest first), computed on the device by a first launch. NULL
+ *              is accepted: every workgroup then ranks the units itself
+ *              (slower start). Only the d = 128 bf16 kernel reads it. Two calls
+ *              that share a workspace must not overlap in time.
  */
 velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v,
                                  velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
                                  int N, int M, int d, float scale, const int32_t* route_ids,
                                  const int32_t* route_len, int L, int include_current,
-                                 void* o, float* lse, void* stream);
+                                 void* o, float* lse, void* workspace, void* stream);
+
+/* Bytes of the workspace of velox_sparse_attn: 16 per (head, pair of query
+ * blocks), i.e. 16 * H * ceil(N / 2); 0 for H < 1, N < 1, L < 1 or d < 1. */
+size_t velox_sparse_attn_workspace_size(int H, int N, int L, int d);
 
 /*
  * velox_dense_attn — the dense baseline ([digest] Prerequisites: dense
@@ -249,9 +262,10 @@ velox_status_t velox_dense_attn(const void* q, const void* k, const void* v,
  * float rounding.
  *   n_split          1 .. VELOX_MAX_SPLIT; 1 is the unsplit call
  *   workspace        device buffer, 16-byte aligned, of at least
- *                    velox_attn_split_workspace_size(H, N, n_split) bytes,
- *                    caller-owned; contents undefined on return; may be NULL
- *                    when n_split = 1
+ *                    velox_attn_split_workspace_size(H, N, n_split) bytes
+ *                    (partial outputs, then, for routed calls, the unit
+ *                    schedule as in velox_sparse_attn), caller-owned; contents
+ *                    undefined on return; may be NULL when n_split = 1
  *   workspace_bytes  its size
  * Other arguments as for the unsplit calls. Rows are split only by the d = 128
  * bf16 kernel with routes of at most 2048 tiles; other shapes run unsplit and

@@ -97,12 +97,13 @@ def test_attention_validation(lib):
     ldq, ldkv = N * 128 * d, (M + N) * 128 * d
     s = ctypes.c_float(0.125)
     A = 0x10000  # aligned fake pointer
-    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, 80, s, A, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
-    assert sp(A, A, A, 1, ldq, ldkv - 1, H, N, M, d, s, A, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
-    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, None, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
-    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 0, 1, A, None, None) == _lib.VELOX_ERR_INVALID
-    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 2, A, None, None) == _lib.VELOX_ERR_INVALID
-    assert sp(A + 2, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, 80, s, A, A, 16, 1, A, None, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv - 1, H, N, M, d, s, A, A, 16, 1, A, None, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, None, A, 16, 1, A, None, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 0, 1, A, None, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 2, A, None, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A + 2, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 1, A, None, None, None) == _lib.VELOX_ERR_INVALID
+    assert sp(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 1, A, None, A + 8, None) == _lib.VELOX_ERR_INVALID
     assert de(A, A, A, 1, ldq, ldkv, H, N, M, d, ctypes.c_float(-1.0), A, None, None) == _lib.VELOX_ERR_INVALID
     assert de(A, A, A, 1, ldq, ldkv, 0, N, M, d, s, A, None, None) == _lib.VELOX_ERR_INVALID
     assert de(None, A, A, 1, ldq, ldkv, H, N, M, d, s, A, None, None) == _lib.VELOX_ERR_INVALID
@@ -115,7 +116,10 @@ def test_split_attention_validation(lib):
     s = ctypes.c_float(0.125)
     A = 0x10000  # aligned fake pointer
     need = lib.velox_attn_split_workspace_size(H, N, 3)
-    assert need == 3 * H * N * 128 * 130 * 4
+    assert need == 3 * H * N * 128 * 130 * 4 + 3 * H * ((N + 1) // 2) * 16
+    assert lib.velox_sparse_attn_workspace_size(H, N, 16, d) == H * ((N + 1) // 2) * 16
+    assert lib.velox_sparse_attn_workspace_size(H, 5, 16, d) == H * 3 * 16
+    assert lib.velox_sparse_attn_workspace_size(0, N, 16, d) == 0
     assert lib.velox_attn_split_workspace_size(0, N, 3) == 0
     bad = [
         (0, A, need),                                 # n_split out of range

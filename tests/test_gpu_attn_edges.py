@@ -3,7 +3,8 @@ benchmark does not reach: an odd number of query blocks (a workgroup whose
 second team has no block), rows with no tile at all, attention without the
 current chunk, and more query blocks than the in-kernel longest-first ordering
 stages (its plain-order fallback). Rows are compared with the float64 oracle
-at the bf16 tolerance."""
+at the bf16 tolerance. The unit schedule written to the workspace changes no
+output bit against the in-kernel ranking used without one."""
 
 import numpy as np
 import pytest
@@ -11,6 +12,7 @@ import torch
 
 import geometry_routed_block_amd as velox
 import oracle
+import synth
 from gpu_common import LSE_ATOL, O_ATOL, say, to_np
 
 pytestmark = pytest.mark.gpu
@@ -79,3 +81,45 @@ def test_many_query_blocks_plain_order_fallback():
     rows = [(0, int(i)) for i in rng.choice(N, 12, replace=False)] + [(0, int(np.argmax(lens[0])))]
     _check(q, k, v, o, lse, routes, rows, M, N, False)
     assert torch.isfinite(o.float()).all()
+
+
+def _raw_sparse(q, k, v, ids, lens, M, workspace):
+    """velox_sparse_attn through the C ABI with an explicit (possibly NULL) workspace."""
+    import ctypes
+    from geometry_routed_block_amd import _lib
+    H, NT, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(H, NT, dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    _lib.check(lib.velox_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _lib.VELOX_BF16,
+                                     q.stride(0), k.stride(0), H, NT // 128, M, d,
+                                     ctypes.c_float(1.0 / d ** 0.5), ids.data_ptr(), lens.data_ptr(),
+                                     ids.shape[-1], 1, o.data_ptr(), lse.data_ptr(),
+                                     None if workspace is None else workspace.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("wlname,N", [("chunk48", 36), ("wan13", 35)])
+def test_unit_plan_matches_in_kernel_ranking_bitwise(wlname, N):
+    """The unit schedule written into the workspace only decides which rows
+    share a workgroup and when they run: outputs are bitwise those of the
+    call without a workspace (every workgroup ranking the units itself)."""
+    wl = synth.chunk48() if wlname == "chunk48" else synth.wan13()
+    say(f"unit plan vs in-kernel ranking on {wlname}, N={N}")
+    q, k, v = synth.make_qkv(wl, device=DEV)
+    q = q[:, : N * 128].contiguous()
+    kbar = velox.block_mean(k[:, : wl.M * 128])
+    p = velox.route_scores(q, kbar, wl.M)
+    g = torch.from_numpy(wl.g[:N]).to(DEV)
+    rho = torch.from_numpy(wl.rho[:N]).to(DEV)
+    coord = torch.from_numpy(np.ascontiguousarray(
+        np.concatenate([wl.coords[: wl.M], wl.coords[wl.M: wl.M + N]]), np.int32)).to(DEV)
+    ids, lens = velox.route_select(p, g, rho, coord, wl.params)
+    ws = velox.attn_workspace(q, ids.shape[-1])
+    o1, l1 = _raw_sparse(q, k, v, ids, lens, wl.M, ws)
+    o0, l0 = _raw_sparse(q, k, v, ids, lens, wl.M, None)
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    o2, l2 = velox.sparse_attn(q, k, v, ids, lens, wl.M, want_lse=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
