@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/velox.h"
@@ -83,6 +84,44 @@ static velox_status_t check_geometry_sizes(int N, int M) {
   REQUIRE(N <= 65535, "N=%d exceeds 65535", N);
   return VELOX_OK;
 }
+
+// ---------------------------------------------------------------- no-allocation entry
+
+// The unit plan of velox_sparse_attn_noalloc: a fixed array in the global
+// memory of every device the library runs on, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// stands for a host-side shadow, not a device address); it uses the device
+// address resolved once per device below.
+static __device__ __align__(256) int4 scratch[VELOX_NOALLOC_MAX_UNITS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (hipGetSymbolAddress
+// on the first call on a device, with that device current; cached after).
+velox_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VELOX_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VELOX_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(VELOX_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  e != hipSuccess ? hipGetErrorString(e) : "null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VELOX_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -257,6 +296,32 @@ velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v, ve
   return sparse_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, route_ids, route_len, L,
                        include_current, o, lse, stream, false, "velox_sparse_attn", 1, nullptr, 0,
                        workspace);
+}
+
+
+velox_status_t velox_sparse_attn_noalloc(const void* q, const void* k, const void* v,
+                                         velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                         int N, int M, int d, float scale,
+                                         const int32_t* route_ids, const int32_t* route_len,
+                                         int L, int include_current, void* o, float* lse,
+                                         void* stream) {
+  // every check before the first HIP call: a rejected call touches no device
+  velox_status_t st = check_attn(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, o);
+  if (st != VELOX_OK) return st;
+  REQUIRE(route_ids && route_len, "route_ids and route_len must be non-NULL");
+  REQUIRE(L >= 1, "L must be >= 1");
+  REQUIRE(include_current == 0 || include_current == 1, "include_current must be 0 or 1");
+  const size_t need = velox::attn_plan_bytes(H, N, 1);
+  if (need > sizeof(scratch))
+    return fail(VELOX_ERR_UNSUPPORTED,
+                "H * ceil(N / 2) = %zu units exceed the %d of the no-allocation scratch (%zu bytes)",
+                need / sizeof(int4), VELOX_NOALLOC_MAX_UNITS, sizeof(scratch));
+  void* plan = nullptr;
+  st = scratch_address(&plan);
+  if (st != VELOX_OK) return st;
+  return sparse_common(q, k, v, dt, ld_q_h, ld_kv_h, H, N, M, d, scale, route_ids, route_len, L,
+                       include_current, o, lse, stream, false, "velox_sparse_attn_noalloc", 1,
+                       nullptr, 0, plan);
 }
 
 velox_status_t velox_sparse_attn_shared(const void* q, const void* k, const void* v,

@@ -240,6 +240,29 @@ velox_status_t velox_sparse_attn(const void* q, const void* k, const void* v,
 size_t velox_sparse_attn_workspace_size(int H, int N, int L, int d);
 
 /*
+ * velox_sparse_attn_noalloc — velox_sparse_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments and results as
+ * velox_sparse_attn without the workspace: the unit schedule goes to a fixed
+ * array in the library's device memory (VELOX_NOALLOC_MAX_UNITS entries of 16
+ * bytes = 1 MiB per device, held until the process ends; its address is
+ * resolved once per device, on the first call with that device current).
+ * The call allocates nothing and calls no allocating routine.
+ * Limit: H * ceil(N / 2) <= VELOX_NOALLOC_MAX_UNITS, else VELOX_ERR_UNSUPPORTED
+ * (checked on the host, nothing launched). Every call on a device shares that
+ * device's array: two calls on one device that overlap in time (different
+ * streams, or host threads) race and must not be issued. Nothing in the
+ * array needs clearing: each call writes every entry it reads.
+ */
+#define VELOX_NOALLOC_MAX_UNITS 65536
+velox_status_t velox_sparse_attn_noalloc(const void* q, const void* k, const void* v,
+                                         velox_dtype_t dt, int64_t ld_q_h, int64_t ld_kv_h, int H,
+                                         int N, int M, int d, float scale,
+                                         const int32_t* route_ids, const int32_t* route_len,
+                                         int L, int include_current, void* o, float* lse,
+                                         void* stream);
+
+/*
  * velox_dense_attn — the dense baseline ([digest] Prerequisites: dense
  * FlashAttention schedules every current-history tile pair). Same as
  * velox_sparse_attn with every history tile routed and include_current = 1.

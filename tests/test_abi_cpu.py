@@ -109,6 +109,23 @@ def test_attention_validation(lib):
     assert de(None, A, A, 1, ldq, ldkv, H, N, M, d, s, A, None, None) == _lib.VELOX_ERR_INVALID
 
 
+def test_noalloc_attention_rejects_oversized_calls(lib):
+    """The no-allocation entry point checks its fixed scratch limit on the host
+    (nothing launched): H * ceil(N / 2) units of 16 bytes must fit."""
+    na = lib.velox_sparse_attn_noalloc
+    d, M, s, A = 128, 16, ctypes.c_float(0.125), 0x10000
+    for H, N, ok in ((1, 131073, False), (2, 65537, False), (1, 131072, True)):
+        if ok:
+            continue   # a call within the limit would launch: GPU tests cover it
+        ldq, ldkv = N * 128 * d, (M + N) * 128 * d
+        assert na(A, A, A, 1, ldq, ldkv, H, N, M, d, s, A, A, 16, 1, A, None, None) == \
+            _lib.VELOX_ERR_UNSUPPORTED
+        assert b"no-allocation" in lib.velox_last_error()
+    H, N = 2, 4
+    ldq, ldkv = N * 128 * d, (M + N) * 128 * d
+    assert na(A, A, A, 1, ldq, ldkv, H, N, M, d, s, None, A, 16, 1, A, None, None) == _lib.VELOX_ERR_INVALID
+
+
 def test_split_attention_validation(lib):
     sp, de = lib.velox_sparse_attn_split, lib.velox_dense_attn_split
     H, N, M, d = 2, 4, 16, 128
