@@ -72,6 +72,11 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the chunk-48 step, time the routed step and dense attention at the "
                          "chunk-48 shape with 0%%, 50%% and 100%% of the query blocks covered")
+    ap.add_argument("--trace-layers", type=int, default=3,
+                    help="layers (seeds 1000 + l) of the compact rollout trace folded into the default "
+                         "JSON line (chunks 1, 2, 4, 7, 12, 24, 48); 0 skips it")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 0/50/100%% coverage sweep of the default JSON line")
     return ap.parse_args()
 
 
@@ -151,6 +156,110 @@ def run_trace(args):
                       "first_chunk_routed_faster": cross, "trace": rows}), flush=True)
 
 
+def _timed(fn, warm, reps):
+    """Mean ms of `reps` back-to-back calls after `warm` untimed ones."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _routed_case(velox, q, k, v, kbar, wl, dev):
+    """Buffers and the routed step (importance, routes, sparse attention) of a
+    workload whose KV may be a prefix of a larger cache."""
+    import numpy as np
+    import torch
+    M = wl.M
+    g = torch.from_numpy(wl.g).to(dev)
+    rho = torch.from_numpy(wl.rho).to(dev)
+    coord = torch.from_numpy(np.ascontiguousarray(wl.coords, np.int32)).to(dev)
+    L = velox.route_bound(wl.params, M)
+    p = torch.zeros(wl.H, wl.N, M, dtype=torch.float32, device=dev)
+    ids = torch.empty(wl.H, wl.N, L, dtype=torch.int32, device=dev)
+    lens = torch.empty(wl.H, wl.N, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    ws = velox.attn_workspace(q, L)
+
+    def step():
+        if M > 0:
+            velox.route_scores(q, kbar, M, out=p)
+        velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
+        velox.sparse_attn(q, k, v, ids, lens, M, out=o, workspace=ws)
+    return step, lens, o
+
+
+def compact_trace(layers, dev):
+    """Routed step vs dense attention along the rollout, folded into the default
+    line: chunks 1, 2, 4, 7, 12, 24, 48 of `layers` layers (seeds 1000 + l). Per
+    layer one KV cache of 1728 blocks is drawn and chunk c uses its first
+    36 c blocks (36 (c - 1) history blocks + the current chunk)."""
+    import numpy as np
+    import torch
+    import geometry_routed_block_amd as velox
+    import synth
+    chunks = [1, 2, 4, 7, 12, 24, 48]
+    routed = np.zeros((layers, len(chunks)))
+    dense = np.zeros((layers, len(chunks)))
+    tiles = np.zeros((layers, len(chunks)), np.int64)
+    for ell in range(layers):
+        full = synth.trace_chunk(48, ell)
+        q, k, v = synth.make_qkv(full, device=dev)
+        kbar = velox.block_mean(k[:, : full.M * 128])
+        od = torch.empty_like(q)
+        for ci, c in enumerate(chunks):
+            wl = full if c == 48 else synth.trace_chunk(c, ell)
+            T = (wl.M + wl.N) * 128
+            kc, vc = k[:, :T], v[:, :T]
+            step, lens, _ = _routed_case(velox, q, kc, vc, kbar, wl, dev)
+            routed[ell, ci] = _timed(step, 3, 10)
+            dense[ell, ci] = _timed(lambda: velox.dense_attn(q, kc, vc, wl.M, out=od), 1, 3)
+            tiles[ell, ci] = int((lens.cpu().numpy() + wl.N).sum())
+        log(f"trace layer {ell}: routed {np.round(routed[ell], 3).tolist()} dense {np.round(dense[ell], 3).tolist()}")
+        del q, k, v, kbar, od
+        torch.cuda.empty_cache()
+    r_med, d_med = np.median(routed, axis=0), np.median(dense, axis=0)
+    cross = next((c for c, r, d in zip(chunks, r_med, d_med) if r < d), None)
+    return {"layers": layers, "seeds": [1000 + ell for ell in range(layers)], "chunks": chunks,
+            "history_blocks": [36 * (c - 1) for c in chunks],
+            "routed_ms": [round(float(x), 4) for x in r_med], "dense_ms": [round(float(x), 4) for x in d_med],
+            "speedup": [round(float(d / r), 3) for r, d in zip(r_med, d_med)],
+            "tiles_visited": [int(x) for x in np.median(tiles, axis=0)],
+            "first_chunk_routed_faster": cross,
+            "routed_ms_by_layer": [[round(float(x), 4) for x in row] for row in routed]}
+
+
+def compact_sweep(dev):
+    """Routed step vs dense at the chunk-48 shape with 0%, 50% and 100% of the
+    query blocks covered (seeds 480-482)."""
+    import torch
+    import geometry_routed_block_amd as velox
+    import synth
+    out = {}
+    for frac in (0.0, 0.5, 1.0):
+        wl = synth.sweep(frac)
+        q, k, v = synth.make_qkv(wl, device=dev)
+        kbar = velox.block_mean(k[:, : wl.M * 128])
+        step, lens, _ = _routed_case(velox, q, k, v, kbar, wl, dev)
+        r = _timed(step, 3, 10)
+        od = torch.empty_like(q)
+        d = _timed(lambda: velox.dense_attn(q, k, v, wl.M, out=od), 1, 3)
+        tiles = int((lens.cpu().numpy() + wl.N).sum())
+        out[f"{int(frac * 100)}%"] = {"routed_ms": round(r, 4), "dense_ms": round(d, 4),
+                                      "speedup": round(d / r, 3), "tiles_visited": tiles,
+                                      "eff_tflops": round(4.0 * 128 ** 3 * tiles / (r * 1e-3) / 1e12, 1)}
+        log(f"sweep covered {int(frac * 100)}%: routed {r:.3f} ms, dense {d:.3f} ms ({d / r:.2f}x)")
+        del q, k, v, kbar, od
+        torch.cuda.empty_cache()
+    return out
+
+
 def unique_tile_count(ids, lens, N, M):
     """Distinct (head, tile) pairs the sparse kernel reads (routed + current chunk)."""
     import numpy as np
@@ -164,59 +273,92 @@ def unique_tile_count(ids, lens, N, M):
     return total
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, q, k, v, p, ids, lens, seconds, max_rows=4096):
-    """Oracle timed on a bounded sample, extrapolated to one whole call."""
+    """The oracle timed on a bounded sample, extrapolated to one whole call:
+    importance and routes of one head, attention of rows drawn from every head
+    (their tiles gathered to host memory outside the timed part), once with the
+    BLAS pool as numpy sets it up and once on one thread."""
     import numpy as np
-    import torch
 
     import oracle
-
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        threadpool_limits = None
+        blas = 1
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = nproc
     rng = np.random.default_rng(0)
-    heads = [0, 1]
-    qn = q[heads].float().cpu().numpy()
-    kn = k[heads].float().cpu().numpy()
-    vn = v[heads].float().cpu().numpy()
-    p_np = p[heads].cpu().numpy()
+
+    qn0 = q[0:1].float().cpu().numpy()
+    kn0 = k[0:1, : wl.M * 128].float().cpu().numpy()
+    p_np = p[0].cpu().numpy()
     ids_np, lens_np = ids.cpu().numpy(), lens.cpu().numpy()
-
     t0 = time.perf_counter()
-    qb = oracle.block_means(qn[:1])
-    kb = oracle.block_means(kn[:1, : wl.M * 128])
-    oracle.importance(qb, kb, wl.scale)
+    oracle.importance(oracle.block_means(qn0), oracle.block_means(kn0), wl.scale)
     t_imp = time.perf_counter() - t0
-
+    del kn0
     t0 = time.perf_counter()
     for i in range(wl.N):
-        oracle.route_row(p_np[0, i], wl.g[i], wl.rho[i], wl.params, wl.M, wl.coords, i)
+        oracle.route_row(p_np[i], wl.g[i], wl.rho[i], wl.params, wl.M, wl.coords, i)
     t_route = time.perf_counter() - t0
 
-    # random (head, block) rows of the two sampled heads, drawn with replacement
-    # until the time budget is spent (at least 8, at most max_rows)
-    t0 = time.perf_counter()
-    done = 0
-    while done < max_rows and (done < 8 or time.perf_counter() - t0 < seconds):
-        h, i = int(rng.integers(0, 2)), int(rng.integers(0, wl.N))
-        route = ids_np[heads[h], i, : lens_np[heads[h], i]].tolist()
-        oracle.sparse_attention_block(qn, kn, vn, wl.scale, h, i, route, wl.M, wl.N)
-        done += 1
-    t_attn = time.perf_counter() - t0
-    rows_n = done
+    def gather(h, i):
+        """Row (h, i) with its tiles (route, then the current chunk) packed."""
+        import torch
+        tiles = ids_np[h, i, : lens_np[h, i]].tolist() + list(range(wl.M, wl.M + wl.N))
+        idx = torch.tensor(tiles, device=k.device)
+        kt = k[h].view(-1, 128, k.shape[-1])[idx].reshape(1, -1, k.shape[-1])
+        vt = v[h].view(-1, 128, v.shape[-1])[idx].reshape(1, -1, v.shape[-1])
+        return (q[h:h + 1, i * 128:(i + 1) * 128].float().cpu().numpy(), kt.float().cpu().numpy(),
+                vt.float().cpu().numpy(), len(tiles))
+
+    def sample(budget, limit):
+        done, spent = 0, 0.0
+        while done < limit and (done < 8 or spent < budget):
+            h, i = int(rng.integers(0, wl.H)), int(rng.integers(0, wl.N))
+            qs, ks, vs, T = gather(h, i)
+            t1 = time.perf_counter()
+            oracle.attention_block(qs, ks, vs, wl.scale, 0, 0, range(T))
+            spent += time.perf_counter() - t1
+            done += 1
+        return done, spent
+
+    rows_n, t_attn = sample(seconds, max_rows)
     n_rows = wl.H * wl.N
     total_s = wl.H * t_imp + wl.H * t_route + n_rows / rows_n * t_attn
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            r1, t1 = sample(min(seconds, 8.0), 64)
+        one = wl.H * t_imp + wl.H * t_route + n_rows / r1 * t1   # importance/routes barely use BLAS
     return {
         "value": round(total_s * 1e3, 1),
         "unit": "ms",
-        "cores": int(cores),
+        "cores": int(blas),
         "kind": "oracle",
-        "sample": (f"importance of 1 head, routes of the 36 rows of 1 head, sparse attention of "
-                   f"{rows_n} (head, block) rows drawn with replacement from heads 0-1; scaled to "
-                   f"{wl.H} heads x {wl.N} rows "
-                   f"(measured {t_imp + t_route + t_attn:.1f} s of CPU time)"),
+        "sample": (f"importance of 1 head, routes of the {wl.N} rows of 1 head, sparse attention of "
+                   f"{rows_n} (head, block) rows drawn with replacement from all {wl.H} heads; scaled to "
+                   f"{wl.H} heads x {wl.N} rows (measured {t_imp + t_route + t_attn:.1f} s of CPU time)"),
+        "nproc": int(nproc),
+        "affinity_cpus": int(affinity),
+        "cpu_model": _cpu_model(),
+        "value_1core_ms": round(one * 1e3, 1) if one is not None else None,
     }
 
 
@@ -268,6 +410,12 @@ def main():
         velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
         velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o, workspace=ws)
 
+    # the rollout trace and the coverage sweep run first, so that the headline
+    # warmup starts on a GPU that is already busy (after an idle period the
+    # attention kernel runs slower for about its first ten launches)
+    trace = compact_trace(args.trace_layers, dev) if args.trace_layers > 0 else None
+    sweep = None if args.no_sweep else compact_sweep(dev)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -295,6 +443,27 @@ def main():
     t_sparse = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     log(f"timed {K} steps: {ms_per_step:.3f} ms/step (scores {t_scores:.3f}, select {t_select:.3f}, "
         f"sparse {t_sparse:.3f})")
+
+    # the same step with cold caches: 512 MiB written before each step (more
+    # than the 8 x 4 MiB L2 and the 256 MiB MALL), outside the timed events
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    cold = []
+    for s in range(K):
+        flush.fill_(float(s))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        velox.route_scores(q, kbar, wl.M, out=p)
+        e[1].record()
+        velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
+        e[2].record()
+        velox.sparse_attn(q, k, v, ids, lens, wl.M, out=o, workspace=ws)
+        e[3].record()
+        torch.cuda.synchronize()
+        cold.append([e[0].elapsed_time(e[3]), e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
+                     e[2].elapsed_time(e[3])])
+    del flush
+    cold = np.median(np.array(cold), axis=0)
+    log(f"cold caches: {cold[0]:.3f} ms/step (scores {cold[1]:.3f}, select {cold[2]:.3f}, sparse {cold[3]:.3f})")
 
     # the same step captured once in a HIP graph and replayed (no host launch
     # work per step)
@@ -501,6 +670,12 @@ def main():
         "pct_mfma_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
         "breakdown_ms": {"route_scores": round(t_scores, 4), "route_select": round(t_select, 4),
                          "sparse_attn": round(t_sparse, 4)},
+        "cold_cache": {"ms_per_step": round(float(cold[0]), 4),
+                       "breakdown_ms": {"route_scores": round(float(cold[1]), 4),
+                                        "route_select": round(float(cold[2]), 4),
+                                        "sparse_attn": round(float(cold[3]), 4)},
+                       "note": "median over the timed steps, each after a 512 MiB overwrite that evicts "
+                               "L2 and MALL"},
         "ms_per_step_graph_replay": round(graph_ms, 4),
         "dense_ms": round(dense_ms, 4),
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
@@ -515,6 +690,10 @@ def main():
                                  "multiwarp_samples": int(fr.numel())},
         "tiles_visited": tiles,
         "history_flop_share": round(flop_hist / flop, 4),
+        "rollout_trace": trace,
+        "coverage_sweep": sweep,
+        "order": ("rollout trace and coverage sweep, then the headline warmup and timed steps, then the "
+                  "cold-cache steps, graph replay, dense baseline and side measurements"),
         "roofline": {
             "bound": "mfma",
             "achieved": round(kern_tflops, 1),
@@ -524,6 +703,8 @@ def main():
             "traffic": None,
             "traffic_note": None,
             "kernel": "velox::pp::attn_kernel<true> (routed, d 128, bf16)",
+            "timing_note": ("achieved = tile-pair FLOP / mean duration of the velox_sparse_attn call from HIP "
+                            "events on its stream; the call is the unit-plan launch plus the attention kernel"),
             "hbm_unique_bytes": uniq_bytes,
             "hbm_frac_unique": round(uniq_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
