@@ -116,7 +116,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 template <typename T>
 __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x, int64_t ld_x_h,
                                                          int d, float* __restrict__ xbar,
-                                                         int64_t ld_bar_h) {
+                                                         int64_t ld_bar_h, int64_t ld_bar_row) {
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
   __shared__ float part[256 * V];
   const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x
   if (t < d) {
     float tot = 0.f;
     for (int j = 0; j < groups; ++j) tot += part[j * d + t];
-    xbar[h * ld_bar_h + static_cast<int64_t>(b) * d + t] = tot * (1.0f / kBlock);
+    xbar[h * ld_bar_h + static_cast<int64_t>(b) * ld_bar_row + t] = tot * (1.0f / kBlock);
   }
 }
 
@@ -190,7 +190,10 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
 }
 
 // kRaw: write the scaled logits (no softmax) to p, for the head-shared scores.
-template <typename T, int D, int QB, bool kRaw = false>
+// kPre: the query block means were written into the first D floats of every
+// output row by a block-mean launch (rows of M >= D floats); the workgroup
+// reads them back before it overwrites its rows.
+template <typename T, int D, int QB, bool kRaw = false, bool kPre = false>
 __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
     const T* __restrict__ q, int64_t ld_q_h, const float* __restrict__ kbar, int64_t ld_kbar_h,
     int H, int N, int M, float scale, float* __restrict__ p) {
@@ -209,95 +212,114 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   const int h = wg / groups, i0 = (wg % groups) * QB, t = threadIdx.x;
   const int nq = min(QB, N - i0);
 
-  // 1. query block means. Blocks past the group's last re-read the last block
-  // (no branch around the loads); their sums are not stored.
-  constexpr int kLpr = D / 8, kRpw = kWave / kLpr;
+  // history rows of step 2: a group of kLpr lanes shares a row, each lane
+  // holding kDpl consecutive dims (d = 128: 8 lanes of 16 dims; d = 64: 8 of 8)
+  constexpr int kDpl = D == 128 ? 16 : 8;
+  constexpr int kLpr = D / kDpl, kRpw = kWave / kLpr;
   constexpr int kRowsPerIt = kRpw * (kScoreThreads / kWave);
+  constexpr int kBatch = kDpl == 16 ? 2 : 4;  // rows per lane group in flight
   const int lane = t % kWave, wv = t / kWave;
   const int j8 = lane % kLpr, rg = lane / kLpr;
-  float acc[QB][8];
-  {
-    const int c8 = t % kCpr, grp = t / kCpr;
+  const float* kb = kbar + h * ld_kbar_h;
+  auto load_row = [&](int r, float (&x)[kDpl]) {
+    const float4* src =
+        reinterpret_cast<const float4*>(kb + static_cast<int64_t>(min(r, M - 1)) * D + j8 * kDpl);
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const T* src = q + h * ld_q_h + static_cast<int64_t>(min(i0 + b, N - 1)) * kBlock * D + c8 * 8;
+    for (int c = 0; c < kDpl / 4; ++c) {
+      const float4 u = src[c];
+      x[4 * c] = u.x; x[4 * c + 1] = u.y; x[4 * c + 2] = u.z; x[4 * c + 3] = u.w;
+    }
+  };
+  const int r_me = wv * kRpw + rg;
+  float kx[kBatch][kDpl];
+
+  if constexpr (kPre) {
+    // first history rows, then the precomputed means of the group's rows
+    if (M > 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+      for (int b = 0; b < kBatch; ++b) load_row(r_me + b * kRowsPerIt, kx[b]);
+    }
+    for (int x = t; x < nq * D; x += kScoreThreads)
+      qbar[x] = p[(static_cast<int64_t>(h) * N + i0 + x / D) * M + x % D];
+    __syncthreads();
+  } else {
+    // 1. query block means: 16-byte loads of all QB blocks issued at once, summed
+    // per lane, across the row groups of a wave by lane swaps, then across waves
+    // in LDS. Blocks past the group's last re-read the last block (no branch
+    // around the loads); their sums are not stored.
+    float acc[QB][8];
+    {
+      const int c8 = t % kCpr, grp = t / kCpr;
 #pragma unroll
-      for (int ps = 0; ps < kPasses; ++ps) {
-        float x[8];
-        load8<T>(src + (ps * kGroups + grp) * D, x);
+      for (int b = 0; b < QB; ++b) {
+        const T* src = q + h * ld_q_h + static_cast<int64_t>(min(i0 + b, N - 1)) * kBlock * D + c8 * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[b][e] += x[e];
+        for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+#pragma unroll
+        for (int ps = 0; ps < kPasses; ++ps) {
+          float x[8];
+          load8<T>(src + (ps * kGroups + grp) * D, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[b][e] += x[e];
+        }
       }
     }
-  }
-  // first history rows of step 2 (rows past the end load the last row; their
-  // dot products are not stored)
-  const float* kb = kbar + h * ld_kbar_h;
-  auto load_row = [&](int r, float (&x)[8]) {
-    const float4* src =
-        reinterpret_cast<const float4*>(kb + static_cast<int64_t>(min(r, M - 1)) * D + j8 * 8);
-    const float4 u = src[0], v = src[1];
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-  };
-  constexpr int kBatch = 4;  // rows per lane group in flight
-  const int r_me = wv * kRpw + rg;
-  float kx[kBatch][8];
-  if (M > 0) {
+    // first history rows of step 2 (rows past the end load the last row; their
+    // dot products are not stored)
+    if (M > 0) {
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) load_row(r_me + b * kRowsPerIt, kx[b]);
-  }
-  {
-    // the lanes of a wave holding the same chunk (lane mod kCpr) differ in
-    // bits 3 (D = 64), 4 and 5: swap-and-add over those bits, ascending
-    const int c8 = t % kCpr;
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[b][e];
-        if constexpr (kCpr == 8) {
-          const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false);  // row_ror:8
-          v += __int_as_float(y);
-        }
-        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-        acc[b][e] = v;
-      }
-    if (lane < kCpr) {
+      for (int b = 0; b < kBatch; ++b) load_row(r_me + b * kRowsPerIt, kx[b]);
+    }
+    {
+      // the lanes of a wave holding the same chunk (lane mod kCpr) differ in
+      // bits 3 (D = 64), 4 and 5: swap-and-add over those bits, ascending
+      const int c8 = t % kCpr;
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[(wv * QB + b) * D + c8 * 8 + e] = acc[b][e];
+        for (int e = 0; e < 8; ++e) {
+          float v = acc[b][e];
+          if constexpr (kCpr == 8) {
+            const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false);  // row_ror:8
+            v += __int_as_float(y);
+          }
+          const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+          v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+          const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+          v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+          acc[b][e] = v;
+        }
+      if (lane < kCpr) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) red[(wv * QB + b) * D + c8 * 8 + e] = acc[b][e];
+      }
+      __syncthreads();
+      for (int x = t; x < nq * D; x += kScoreThreads) {
+        const int b = x / D, d = x % D;
+        float sum = 0.f;
+        for (int w2 = 0; w2 < kWaves; ++w2) sum += red[(w2 * QB + b) * D + d];
+        qbar[x] = sum * (1.0f / kBlock);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int x = t; x < nq * D; x += kScoreThreads) {
-      const int b = x / D, d = x % D;
-      float sum = 0.f;
-      for (int w2 = 0; w2 < kWaves; ++w2) sum += red[(w2 * QB + b) * D + d];
-      qbar[x] = sum * (1.0f / kBlock);
-    }
-    __syncthreads();
   }
 
-  // 2. logits. The lanes of a group of kLpr = D / 8 lanes share one history
-  // row: lane j8 loads its 8 dims (a row is read contiguously by its group)
-  // and dots them with the same 8 dims of every query mean, which it keeps in
-  // registers; DPP adds then sum the group's partials (every lane ends with
-  // the row's dot products). The loads of the next kBatch rows are issued
-  // before the arithmetic of the current ones.
-  float qv[QB][8];
+  // 2. logits. The lanes of a group share one history row: lane j8 loads its
+  // kDpl dims (a row is read contiguously by its group) and dots them with the
+  // same dims of every query mean, which it keeps in registers; DPP adds then
+  // sum the group's partials (every lane ends with the row's dot products). The
+  // loads of the next kBatch rows are issued before the arithmetic of the
+  // current ones.
+  float qv[QB][kDpl];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + j8 * 8 + e] : 0.f;
+    for (int e = 0; e < kDpl; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + j8 * kDpl + e] : 0.f;
   float lmax = -INFINITY;  // running maximum of the logits this lane stores
   for (int r0 = 0; r0 < M; r0 += kBatch * kRowsPerIt) {
-    float nx[kBatch][8];
+    float nx[kBatch][kDpl];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) load_row(r0 + (kBatch + b) * kRowsPerIt + r_me, nx[b]);
 #pragma unroll
@@ -308,7 +330,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
       for (int qb = 0; qb < QB; ++qb) {
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(qv[qb][e], kx[b][e], acc);
+        for (int e = 0; e < kDpl; ++e) acc = fmaf(qv[qb][e], kx[b][e], acc);
         acc = group_sum<kLpr>(acc);
         if (j8 == qb) mine = acc;
       }
@@ -320,7 +342,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
 #pragma unroll
     for (int b = 0; b < kBatch; ++b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kx[b][e] = nx[b][e];
+      for (int e = 0; e < kDpl; ++e) kx[b][e] = nx[b][e];
   }
   __syncthreads();
 
@@ -858,10 +880,12 @@ hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, in
   dim3 grid(nblk, H);
   if (bf16)
     hipLaunchKernelGGL(block_mean_kernel<bf16_t>, grid, dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(x), ld_x_h, d, xbar, ld_bar_h);
+                       static_cast<const bf16_t*>(x), ld_x_h, d, xbar, ld_bar_h,
+                       static_cast<int64_t>(d));
   else
     hipLaunchKernelGGL(block_mean_kernel<float>, grid, dim3(256), 0, stream,
-                       static_cast<const float*>(x), ld_x_h, d, xbar, ld_bar_h);
+                       static_cast<const float*>(x), ld_x_h, d, xbar, ld_bar_h,
+                       static_cast<int64_t>(d));
   return hipGetLastError();
 }
 
@@ -871,12 +895,23 @@ size_t route_scores_lds_bytes(int qb, int M, int d) {
                           static_cast<size_t>(qb) * M);
 }
 
+// With M >= d the query block means come from a block-mean launch of their
+// own (one workgroup per block: far more loads in flight than the scoring
+// workgroups have) that writes them into the first d floats of each output
+// row; the scoring workgroup of the row reads them before overwriting it.
 template <typename T, int D, int QB, bool kRaw>
 static hipError_t scores_launch(const void* q, int64_t ld_q_h, const float* kbar,
                                 int64_t ld_kbar_h, int H, int N, int M, float scale, float* p,
                                 hipStream_t stream) {
   const size_t lds = route_scores_lds_bytes(QB, M, D);
-  auto kern = route_scores_kernel<T, D, QB, kRaw>;
+  const bool pre = M >= D;
+  if (pre) {
+    hipLaunchKernelGGL(block_mean_kernel<T>, dim3(N, H), dim3(256), 0, stream, static_cast<const T*>(q),
+                       ld_q_h, D, p, static_cast<int64_t>(N) * M, static_cast<int64_t>(M));
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
+  auto kern = pre ? route_scores_kernel<T, D, QB, kRaw, true> : route_scores_kernel<T, D, QB, kRaw, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
