@@ -106,29 +106,38 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
+// Workgroup barrier that waits only for this wave's LDS (and scalar memory)
+// operations: global loads in flight are waited for where their registers are
+// used, not at every barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- block means
 
 // One workgroup (256 threads) per (block, head). Each thread reads 16-byte
 // vectors of one column group from 128 / (256 / vpr) rows (vpr = vectors per
-// row), then the row groups are summed through LDS. Summation order: per
-// thread over its rows in ascending order, then over row groups in ascending
-// order.
-template <typename T>
+// row; all of them requested before the first is added), then the row groups
+// are summed through LDS. Summation order: per thread over its rows in
+// ascending order, then over row groups in ascending order.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x, int64_t ld_x_h,
-                                                         int d, float* __restrict__ xbar,
-                                                         int64_t ld_bar_h, int64_t ld_bar_row) {
+                                                         float* __restrict__ xbar, int64_t ld_bar_h,
+                                                         int64_t ld_bar_row) {
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int kVpr = D / V, kGroups = 256 / kVpr, kRows = kBlock / kGroups;
   __shared__ float part[256 * V];
   const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int vpr = d / V, groups = 256 / vpr;
-  const int cv = t % vpr, g = t / vpr;
-  const T* src = x + h * ld_x_h + static_cast<int64_t>(b) * kBlock * d + cv * V;
+  const int cv = t % kVpr, g = t / kVpr;
+  const T* src = x + h * ld_x_h + static_cast<int64_t>(b) * kBlock * D + cv * V;
+  uint4 u[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k)
+    u[k] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(g + k * kGroups) * D);
   float acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
-  for (int a = g; a < kBlock; a += groups) {
-    const uint4 u = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(a) * d);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
     if constexpr (V == 8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -141,11 +150,11 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x
     }
   }
 #pragma unroll
-  for (int e = 0; e < V; ++e) part[g * d + cv * V + e] = acc[e];
+  for (int e = 0; e < V; ++e) part[g * D + cv * V + e] = acc[e];
   __syncthreads();
-  if (t < d) {
+  if (t < D) {
     float tot = 0.f;
-    for (int j = 0; j < groups; ++j) tot += part[j * d + t];
+    for (int j = 0; j < kGroups; ++j) tot += part[j * D + t];
     xbar[h * ld_bar_h + static_cast<int64_t>(b) * ld_bar_row + t] = tot * (1.0f / kBlock);
   }
 }
@@ -446,13 +455,15 @@ __global__ __launch_bounds__(kScoreThreads) void head_mean_softmax_kernel(
 //     ascending key order ranks by w descending, then id ascending (w >= 0);
 //     the keys are distinct.
 //  2. the `limit` smallest keys (limit = the cap): a radix select, 8 bits at a
-//     time from the top, finds the bucket of the limit-th smallest key, the
+//     time from the top, finds the bucket of the limit-th smallest key (the
+//     first histogram, of the top byte, is made while the keys are built), the
 //     keys up to it are gathered and, when a mass cut follows, put in order by
 //     counting for each the keys below it. (A cap above kFastSel falls back to
 //     a bitonic sort of all keys.)
 //  3. count c of taken candidates: the cap, or the first prefix whose mass
 //     meets the threshold (block-wide scan of the ordered masses).
-//  4. route = reserved ∪ first c ∪ safeguards as an LDS bitmask; emit ascending.
+//  4. route = reserved ∪ first c ∪ safeguards as an LDS bitmask; emit ascending
+//     (every set bit writes its id at its rank among the set bits).
 // Inputs outside what the fixed-point mass allows are reported per row in the
 // optional status word: an entry of p that is negative, NaN or infinite, an
 // entry of g outside [0, 1] (NaN included), or, on a row with a mass cut, a
@@ -471,6 +482,7 @@ struct SelectArgs {
   int32_t* status;  // nullable: [0] rows with bad inputs, [1] smallest such row
   int N, M, L, P2, nwords;
   int fs;  // capacity of the selected-key buffers: the largest radix-select cap
+  int vec;  // rows read as 16-byte vectors: M % 4 == 0, p, g (and coord) 16-byte aligned
   float tau, g_ref, lambda, eta_cov, theta_cov, theta_unc;
   int K_cov, K_unc, n_prev, neigh26, n_ref, mode;
 };
@@ -506,6 +518,19 @@ __device__ __forceinline__ bool mass_reached(uint64_t m, uint64_t thq, uint64_t 
   return lhs_hi > rhs_hi || (lhs_hi == rhs_hi && lhs_lo >= rhs_lo);
 }
 
+// hist[bin] += number of active lanes with `on` and that bin: one LDS atomic
+// per distinct bin of the wave (the top byte of the keys takes few values).
+__device__ __forceinline__ void count_by_wave(int* hist, uint32_t bin, bool on) {
+  uint64_t pend = __ballot(on);
+  while (pend) {
+    const int lead = __builtin_ffsll(static_cast<long long>(pend)) - 1;
+    const uint32_t b = __builtin_amdgcn_readlane(bin, lead);
+    const uint64_t same = __ballot(on && bin == b);
+    if (static_cast<int>(threadIdx.x % kWave) == lead) atomicAdd(&hist[b], __popcll(same));
+    pend &= ~same;
+  }
+}
+
 __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs a) {
   extern __shared__ uint64_t sel_smem[];
   const int fs = a.fs;
@@ -514,8 +539,8 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   uint64_t* ordered = sel + fs;                                   // [fs]
   uint64_t* red64 = ordered + fs;                                 // [3 * 8 waves + 1]
   SelectCtl* ctl = reinterpret_cast<SelectCtl*>(red64 + 25);
-  int* hist = reinterpret_cast<int*>(ctl + 1);                    // [256]
-  uint32_t* mask = reinterpret_cast<uint32_t*>(hist + 256);       // [nwords]
+  int* hist = reinterpret_cast<int*>(ctl + 1);                    // [2][256]
+  uint32_t* mask = reinterpret_cast<uint32_t*>(hist + 512);       // [nwords]
   int* wscan = reinterpret_cast<int*>(mask + a.nwords);           // [8 waves + 2]
 
   const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x, nt = blockDim.x;
@@ -527,14 +552,22 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   const int n_res = min(a.n_prev, M);
   const int res0 = M - n_res;
 
+  // cleared before any use: route mask, both radix histograms, flag word, gather count
   for (int wd = t; wd < a.nwords; wd += nt) mask[wd] = 0u;
+  for (int b = t; b < 512; b += nt) hist[b] = 0;
+  if (t == 0) {
+    red64[24] = 0;
+    ctl->n = 0;
+  }
+  lds_barrier();
 
-  // 1. weights, masses, keys. The loads of kChunk rows per thread are issued
-  // before their arithmetic (rows past the end re-read the last row). The
-  // 26-neighbour test of the same rows is kept in `nbits` (bit k: the k-th row
-  // of this thread) and entered in the mask after the barrier below, when the
-  // clear above has completed; threads with more than 32 rows test later.
-  constexpr int kChunk = 4;
+  // 1. weights, masses, keys, and the histogram of the keys' top byte (the
+  // radix select's first pass). The loads of kChunk rows per thread are all
+  // issued before their arithmetic, with no branch between them (rows past
+  // the end re-read the last row). The 26-neighbour test of the same rows is
+  // kept in `nbits` (bit k: the k-th row of this thread) and entered in the
+  // mask after the next barrier; threads with more than 32 rows test later.
+  constexpr int kChunk = 8;
   const bool nb_early = a.neigh26 && a.P2 <= 32 * nt;
   int qt = 0, qh = 0, qw = 0;
   if (a.neigh26) {
@@ -548,60 +581,113 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   uint64_t zhi = 0, zlo = 0, mloc = 0;
   bool bad_in = false, big = false;
   uint32_t nbits = 0;
-  for (int r0 = t, k0 = 0; r0 < a.P2; r0 += kChunk * nt, k0 += kChunk) {
-    float pw[kChunk], gw[kChunk];
-    int cd[kChunk];  // Chebyshev distance of the row's block to the query block
+  // key of row r (bit k of nbits marks it a neighbour); also counted into the
+  // first histogram
+  auto one_key = [&](auto with_nb, int r, float pv, float gv, int cdist, int k) {
+    constexpr bool kNb = decltype(with_nb)::value;
+    uint64_t key = ~0ull;
+    if (r < M) {
+      float w = pv;
+      bad_in |= !(w >= 0.f && w <= 3.402823466e38f) || !(gv >= 0.f && gv <= 1.f);
+      if (covered && a.mode == 0) {
+        const float gh = (gv > a.tau) ? fminf(__fdiv_rn(gv, a.g_ref), 1.0f) : 0.0f;
+        const float uu = __fadd_rn(1.0f, __fmul_rn(a.lambda, gh));
+        w = __fmul_rn(w, uu);
+      } else if (covered && a.mode == 2) {
+        w = gv;
+      }
+      const bool fits = w < 16.f;  // else w 2^60 >= 2^64 (NaN fails too)
+      big |= !fits;
+      const uint64_t W = fits ? fixed_mass(w) : ~0ull;
+      zhi += W >> 32;
+      zlo += W & 0xffffffffull;
+      if (r >= res0)
+        mloc += W;
+      else
+        key = (static_cast<uint64_t>(~__float_as_uint(w)) << 32) | static_cast<uint32_t>(r);
+      if (kNb && cdist == 1) nbits |= 1u << k;
+    }
+    if (r < a.P2) keys[r] = key;
+    count_by_wave(hist, static_cast<uint32_t>(key >> 56), r < M);
+  };
+  auto chebyshev = [&](int ct, int ch, int cw) { return max(abs(ct - qt), max(abs(ch - qh), abs(cw - qw))); };
+  // rows t + u nt of each chunk, 4-byte loads (any M, any alignment)
+  auto build_keys = [&](auto with_nb) {
+    constexpr bool kNb = decltype(with_nb)::value;
+    for (int r0 = t, k0 = 0; r0 < a.P2; r0 += kChunk * nt, k0 += kChunk) {
+      float pw[kChunk], gw[kChunk];
+      int cd[kChunk];  // Chebyshev distance of the row's block to the query block
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      pw[u] = 0.f;
-      gw[u] = 0.f;
-      cd[u] = 0;
-      if (M > 0) {
+      for (int u = 0; u < kChunk; ++u) {
         const int rr = min(r0 + u * nt, M - 1);
         pw[u] = prow[rr];
         gw[u] = grow[rr];
-        if (nb_early) {
+        cd[u] = 0;
+        if constexpr (kNb) {
           const int32_t* rc = a.coord + 3 * static_cast<int64_t>(rr);
-          cd[u] = max(abs(rc[0] - qt), max(abs(rc[1] - qh), abs(rc[2] - qw)));
+          cd[u] = chebyshev(rc[0], rc[1], rc[2]);
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const int r = r0 + u * nt;
-      if (r >= a.P2) break;
-      uint64_t key = ~0ull;
-      if (r < M) {
-        float w = pw[u];
-        bad_in |= !(w >= 0.f && w <= 3.402823466e38f) || !(gw[u] >= 0.f && gw[u] <= 1.f);
-        if (covered && a.mode == 0) {
-          const float g = gw[u];
-          const float gh = (g > a.tau) ? fminf(__fdiv_rn(g, a.g_ref), 1.0f) : 0.0f;
-          const float uu = __fadd_rn(1.0f, __fmul_rn(a.lambda, gh));
-          w = __fmul_rn(w, uu);
-        } else if (covered && a.mode == 2) {
-          w = gw[u];
-        }
-        const bool fits = w < 16.f;  // else w 2^60 >= 2^64 (NaN fails too)
-        big |= !fits;
-        const uint64_t W = fits ? fixed_mass(w) : ~0ull;
-        zhi += W >> 32;
-        zlo += W & 0xffffffffull;
-        if (r >= res0)
-          mloc += W;
-        else
-          key = (static_cast<uint64_t>(~__float_as_uint(w)) << 32) | static_cast<uint32_t>(r);
-        if (nb_early && cd[u] == 1) nbits |= 1u << (k0 + u);
-      }
-      keys[r] = key;
+      for (int u = 0; u < kChunk; ++u) one_key(with_nb, r0 + u * nt, pw[u], gw[u], cd[u], k0 + u);
     }
+  };
+  // rows 4 t .. 4 t + 3 of each quarter chunk, 16-byte loads (M % 4 == 0,
+  // aligned rows); a vector never straddles M, vectors past it re-read the last
+  auto build_keys_vec = [&](auto with_nb) {
+    constexpr bool kNb = decltype(with_nb)::value;
+    constexpr int kVec = kChunk / 4;
+    for (int c0 = 0, k0 = 0; c0 < a.P2; c0 += kChunk * nt, k0 += kChunk) {
+      float4 pv[kVec], gv[kVec];
+      int4 cv[kVec][3];
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        const int rb = min(c0 + v * 4 * nt + 4 * t, M - 4);
+        pv[v] = *reinterpret_cast<const float4*>(prow + rb);
+        gv[v] = *reinterpret_cast<const float4*>(grow + rb);
+        if constexpr (kNb) {
+          const int4* rc = reinterpret_cast<const int4*>(a.coord + 3 * static_cast<int64_t>(rb));
+          cv[v][0] = rc[0];
+          cv[v][1] = rc[1];
+          cv[v][2] = rc[2];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        const int r = c0 + v * 4 * nt + 4 * t;
+        int cd[4] = {0, 0, 0, 0};
+        if constexpr (kNb) {
+          cd[0] = chebyshev(cv[v][0].x, cv[v][0].y, cv[v][0].z);
+          cd[1] = chebyshev(cv[v][0].w, cv[v][1].x, cv[v][1].y);
+          cd[2] = chebyshev(cv[v][1].z, cv[v][1].w, cv[v][2].x);
+          cd[3] = chebyshev(cv[v][2].y, cv[v][2].z, cv[v][2].w);
+        }
+        one_key(with_nb, r, pv[v].x, gv[v].x, cd[0], k0 + 4 * v);
+        one_key(with_nb, r + 1, pv[v].y, gv[v].y, cd[1], k0 + 4 * v + 1);
+        one_key(with_nb, r + 2, pv[v].z, gv[v].z, cd[2], k0 + 4 * v + 2);
+        one_key(with_nb, r + 3, pv[v].w, gv[v].w, cd[3], k0 + 4 * v + 3);
+      }
+    }
+  };
+  if (M > 0) {
+    if (a.vec) {
+      if (nb_early)
+        build_keys_vec(std::true_type{});
+      else
+        build_keys_vec(std::false_type{});
+    } else {
+      if (nb_early)
+        build_keys(std::true_type{});
+      else
+        build_keys(std::false_type{});
+    }
+  } else if (t == 0) {
+    keys[0] = ~0ull;  // P2 = 1
   }
   zhi = wave_sum_u64(zhi);
   zlo = wave_sum_u64(zlo);
   mloc = wave_sum_u64(mloc);
   const bool wave_bad = __ballot(bad_in) != 0, wave_big = __ballot(big) != 0;
-  if (t == 0) red64[24] = 0;
-  __syncthreads();
   if (lane == 0) {
     red64[wv] = zhi;
     red64[8 + wv] = mloc;
@@ -610,7 +696,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
       atomicOr(reinterpret_cast<unsigned long long*>(&red64[24]),
                (wave_bad ? 1ull : 0ull) | (wave_big ? 2ull : 0ull));
   }
-  __syncthreads();
+  lds_barrier();  // keys, masses and the first histogram are complete
   uint64_t zh = 0, zl = 0, m0 = 0;
   for (int j = 0; j < nwv; ++j) {
     zh += red64[j];
@@ -623,7 +709,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   while (nbits) {
     const int k = __ffs(nbits) - 1;
     nbits &= nbits - 1;
-    const int r = t + k * nt;
+    const int r = a.vec ? (k / kChunk) * kChunk * nt + ((k % kChunk) / 4) * 4 * nt + 4 * t + (k % 4) : t + k * nt;
     atomicOr(&mask[r >> 5], 1u << (r & 31));
   }
 
@@ -645,21 +731,25 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     int shift = 64;
     if (limit > 0) {
       int rank = limit - 1;  // rank of the wanted key inside the current bucket
+      // pass p counts into hist[p & 1] and clears the other buffer for pass
+      // p + 1 (its last reader, the scan of pass p - 1, ended at a barrier)
       for (int pass = 0; pass < 8; ++pass) {
         shift -= 8;
-        for (int b = t; b < 256; b += nt) hist[b] = 0;
-        __syncthreads();
-        for (int r = t; r < M; r += nt) {
-          const uint64_t key = keys[r];
-          if (shift == 56 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
-            atomicAdd(&hist[(key >> shift) & 255], 1);
+        int* hc = hist + 256 * (pass & 1);
+        if (pass > 0) {
+          int* hn = hist + 256 * ((pass + 1) & 1);
+          for (int b = t; b < 256; b += nt) hn[b] = 0;
+          for (int r = t; r < M; r += nt) {
+            const uint64_t key = keys[r];
+            if ((key >> (shift + 8)) == (prefix >> (shift + 8))) atomicAdd(&hc[(key >> shift) & 255], 1);
+          }
+          lds_barrier();
         }
-        __syncthreads();
         if (wv == 0) {  // lane l scans bins 4 l .. 4 l + 3
           int c4[4], sum = 0;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            c4[q] = hist[4 * lane + q];
+            c4[q] = hc[4 * lane + q];
             sum += c4[q];
           }
           int incl = sum;
@@ -681,23 +771,31 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
             }
           }
         }
-        __syncthreads();
+        lds_barrier();
         prefix = ctl->prefix;
         rank = ctl->rank;
         if (rank == ctl->cnt - 1) break;  // the whole bucket is taken (uniform)
       }
     }
     // gather the keys whose top 64 - shift bits do not exceed the bucket's:
-    // exactly `limit` of them
-    if (t == 0) ctl->n = 0;
-    __syncthreads();
+    // exactly `limit` of them; one slot reservation per wave and row batch
     if (limit > 0) {
       for (int r = t; r < M; r += nt) {
         const uint64_t key = keys[r];
-        if (key != ~0ull && (key >> shift) <= (prefix >> shift)) sel[atomicAdd(&ctl->n, 1)] = key;
+        const bool take = key != ~0ull && (key >> shift) <= (prefix >> shift);
+        const uint64_t bal = __ballot(take);
+        if (bal != 0) {
+          const int lead = __builtin_ffsll(static_cast<long long>(bal)) - 1;
+          int base = 0;
+          if (lane == lead) base = atomicAdd(&ctl->n, __popcll(bal));
+          base = __builtin_amdgcn_readlane(base, lead);
+          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+          if (take) sel[base + below] = key;
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
     top = sel;
     if (cut) {  // ascending order: each key's position is the number of keys below it
       for (int e = t; e < limit; e += nt) {
@@ -782,8 +880,8 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
   __syncthreads();
 
   // 5. ascending emission: exclusive prefix of the words' popcounts (in the
-  // key buffer, free now), then route slot s takes the s-th set bit: the word
-  // by binary search over the prefixes, the bit by halving the word.
+  // key buffer, free now), then every set bit writes its id at its rank: the
+  // prefix of its word plus the set bits below it in the word.
   int32_t* out = a.route_ids + (static_cast<int64_t>(h) * a.N + i) * a.L;
   int* wpre = reinterpret_cast<int*>(keys);  // [nwords]
   int carry_cnt = 0;
@@ -807,29 +905,14 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(SelectArgs
     carry_cnt += total;
     __syncthreads();
   }
-  for (int sl = t; sl < a.L; sl += nt) {
-    int id = -1;
-    if (sl < carry_cnt) {
-      int lo = 0, hi = a.nwords - 1;  // last word whose prefix is <= sl
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (wpre[mid] <= sl) lo = mid; else hi = mid - 1;
-      }
-      uint32_t bits = mask[lo];
-      int k = sl - wpre[lo], bit = 0;  // k-th set bit of bits
-#pragma unroll
-      for (int width = 16; width > 0; width >>= 1) {
-        const int c = __popc(bits & ((1u << width) - 1u));
-        if (k >= c) {
-          k -= c;
-          bits >>= width;
-          bit += width;
-        }
-      }
-      id = lo * 32 + bit;
+  for (int b = t; b < a.nwords * 32; b += nt) {
+    const uint32_t bits = mask[b >> 5];
+    if ((bits >> (b & 31)) & 1u) {
+      const int sl = wpre[b >> 5] + __popc(bits & ((1u << (b & 31)) - 1u));
+      if (sl < a.L) out[sl] = b;
     }
-    out[sl] = id;
   }
+  for (int sl = carry_cnt + t; sl < a.L; sl += nt) out[sl] = -1;
   if (t == 0) a.route_len[static_cast<int64_t>(h) * a.N + i] = min(carry_cnt, a.L);
 }
 
@@ -875,17 +958,26 @@ static int next_pow2(int x) {
   return p;
 }
 
+template <typename T, int D>
+static void block_mean_launch(const void* x, int64_t ld_x_h, int H, int nblk, float* xbar,
+                              int64_t ld_bar_h, int64_t ld_bar_row, hipStream_t stream) {
+  hipLaunchKernelGGL((block_mean_kernel<T, D>), dim3(nblk, H), dim3(256), 0, stream, static_cast<const T*>(x),
+                     ld_x_h, xbar, ld_bar_h, ld_bar_row);
+}
+
 hipError_t launch_block_mean(const void* x, bool bf16, int64_t ld_x_h, int H, int nblk, int d,
                              float* xbar, int64_t ld_bar_h, hipStream_t stream) {
-  dim3 grid(nblk, H);
-  if (bf16)
-    hipLaunchKernelGGL(block_mean_kernel<bf16_t>, grid, dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(x), ld_x_h, d, xbar, ld_bar_h,
-                       static_cast<int64_t>(d));
-  else
-    hipLaunchKernelGGL(block_mean_kernel<float>, grid, dim3(256), 0, stream,
-                       static_cast<const float*>(x), ld_x_h, d, xbar, ld_bar_h,
-                       static_cast<int64_t>(d));
+  if (bf16) {
+    if (d == 128)
+      block_mean_launch<bf16_t, 128>(x, ld_x_h, H, nblk, xbar, ld_bar_h, d, stream);
+    else
+      block_mean_launch<bf16_t, 64>(x, ld_x_h, H, nblk, xbar, ld_bar_h, d, stream);
+  } else {
+    if (d == 128)
+      block_mean_launch<float, 128>(x, ld_x_h, H, nblk, xbar, ld_bar_h, d, stream);
+    else
+      block_mean_launch<float, 64>(x, ld_x_h, H, nblk, xbar, ld_bar_h, d, stream);
+  }
   return hipGetLastError();
 }
 
@@ -906,8 +998,7 @@ static hipError_t scores_launch(const void* q, int64_t ld_q_h, const float* kbar
   const size_t lds = route_scores_lds_bytes(QB, M, D);
   const bool pre = M >= D;
   if (pre) {
-    hipLaunchKernelGGL(block_mean_kernel<T>, dim3(N, H), dim3(256), 0, stream, static_cast<const T*>(q),
-                       ld_q_h, D, p, static_cast<int64_t>(N) * M, static_cast<int64_t>(M));
+    block_mean_launch<T, D>(q, ld_q_h, H, N, p, static_cast<int64_t>(N) * M, static_cast<int64_t>(M), stream);
     const hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
@@ -981,7 +1072,7 @@ static int select_capacity(int M, const RouteConfig& cfg) {
 size_t route_select_lds_bytes(int M, int fs) {
   const int P2 = next_pow2(M > 0 ? M : 1);
   const int nwords = (M + 31) / 32;
-  return sizeof(uint64_t) * (P2 + 2 * fs + 25) + sizeof(SelectCtl) + sizeof(int) * 256 +
+  return sizeof(uint64_t) * (P2 + 2 * fs + 25) + sizeof(SelectCtl) + sizeof(int) * 512 +
          sizeof(uint32_t) * nwords + sizeof(int) * 16;
 }
 
@@ -1003,6 +1094,8 @@ hipError_t launch_route_select(const float* p, const float* g, const float* rho,
   a.P2 = next_pow2(M > 0 ? M : 1);
   a.nwords = (M + 31) / 32;
   a.fs = select_capacity(M, cfg);
+  auto al16 = [](const void* x) { return reinterpret_cast<uintptr_t>(x) % 16 == 0; };
+  a.vec = M % 4 == 0 && al16(p) && al16(g) && (!cfg.neigh26 || al16(coord)) ? 1 : 0;
   a.tau = cfg.tau;
   a.g_ref = cfg.g_ref;
   a.lambda = cfg.lambda;
