@@ -466,9 +466,39 @@ def main():
     torch.cuda.synchronize()
     cold = [[e[0].elapsed_time(e[3]), e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
             for e in cold_ev]
-    del flush
     cold = np.median(np.array(cold), axis=0)
     log(f"cold caches: {cold[0]:.3f} ms/step (scores {cold[1]:.3f}, select {cold[2]:.3f}, sparse {cold[3]:.3f})")
+
+    # The router calls alone, without the event markers between them that the
+    # breakdown above places around each (a marker costs the stream a few us,
+    # which is large against these calls): R calls back to back between two
+    # events after a GPU spin long enough for the host to queue them all (warm),
+    # and R (flush, call) pairs less R flushes alone (cold).
+    def gpu_per_call(body, R=20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(4_000_000)
+        a.record()
+        for _ in range(R):
+            body()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / R
+
+    def do_scores():
+        velox.route_scores(q, kbar, wl.M, out=p)
+
+    def do_select():
+        velox.route_select(p, g, rho, coord, wl.params, L=L, route_ids=ids, route_len=lens)
+
+    t_flush = min(gpu_per_call(lambda: flush.sum()) for _ in range(3))
+    router_us = {}
+    for name, fn in (("route_scores", do_scores), ("route_select", do_select)):
+        warm = min(gpu_per_call(fn) for _ in range(3))
+        both = min(gpu_per_call(lambda: (flush.sum(), fn())) for _ in range(3))
+        router_us[name] = {"warm": round(warm * 1e3, 2), "cold": round((both - t_flush) * 1e3, 2)}
+    del flush
+    log(f"router calls alone (us): {router_us}")
 
     # the same step captured once in a HIP graph and replayed (no host launch
     # work per step)
@@ -681,6 +711,8 @@ def main():
                                         "sparse_attn": round(float(cold[3]), 4)},
                        "note": "median over the timed steps, each after a 512 MiB read that evicts "
                                "L2 and MALL (leaving them clean)"},
+        "router_us": dict(router_us, method="GPU time per call: 20 calls back to back (warm); 20 (512 MiB read, "
+                                            "call) pairs less 20 reads (cold); no event between the calls"),
         "ms_per_step_graph_replay": round(graph_ms, 4),
         "dense_ms": round(dense_ms, 4),
         "dense_tflops": round(dense_flop / (dense_ms * 1e-3) / 1e12, 1),
