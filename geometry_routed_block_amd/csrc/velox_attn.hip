@@ -567,12 +567,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // short pairs fill the tail of the grid); the order is computed here from the
   // route lengths, staged in route_lds before the route ids use it.
   int* lens_s = &route_lds[0][0];
-  int h, pr, split;
+  int h, pr, split, n_rng = nsp;  // n_rng: ranges of this unit's rows
   if (t < 2) pair_rows[t] = -1;
   if (kRouted && a.plan) {
     const int4 u = a.plan[blockIdx.x];
+    if (u.x < 0) return;  // an empty slot of the plan (the whole workgroup leaves)
     h = u.x;
-    split = u.w;
+    split = u.w & 0xff;
+    n_rng = max(u.w >> 8, 1);
     pr = 0;
     __syncthreads();
     if (t < 2) pair_rows[t] = t == 0 ? u.y : u.z;
@@ -672,7 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // this unit's range [t0, t1) of the row's tile list (the whole list unless
   // rows are split)
   const int t_row = rlen + ncur;
-  const int t_chunk = (t_row + nsp - 1) / nsp;
+  const int t_chunk = (t_row + n_rng - 1) / n_rng;
   const int t0 = min(t_row, split * t_chunk);
   const int S = 2 * (min(t_row, t0 + t_chunk) - t0);  // half-tiles of this team's range
   if (kRouted && i >= 0) {
@@ -999,18 +1001,136 @@ struct PlanArgs {
   int route_head_rows;
   int H, N, M, L, include_current, n_split;
   int4* plan;
+  float* part_ml;  // split rows: (max, sum) of every range, [n_split][H][N*128][2]
 };
 
 constexpr int kPlanThreads = 512;
 constexpr int kPlanLdsInts = 12288;
+constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs in 8 XCDs
+
+// Split rows with a plan: each XCD owns a contiguous range of (head, pair)
+// ids. A pair whose cost (its longer row's tiles) is c is cut into
+// n = min(ceil(c / tau), n_split) ranges, with tau the smallest value for
+// which the XCD's ranges fit one round of its CUs (at most kCusPerXcd units,
+// never fewer than one per pair); the ranges of the XCD go longest first to
+// its ceil(pairs / 8) * n_split slots, and the slots left over hold empty
+// units (head -1), whose workgroups return at once. The ranges a pair does not use get (max, sum) =
+// (-inf, 0), which the merge skips. Returns false when the XCD's rows do not
+// fit in LDS (the caller then cuts every pair into n_split ranges).
+__device__ bool plan_split_adaptive(const PlanArgs& a, int x, int* sh) {
+  const int t = threadIdx.x;
+  const int N = a.N, pairs = (N + 1) / 2, nsp = a.n_split;
+  const int P = a.H * pairs;
+  int pbase, pcnt;
+  xcd_range(x, P, pbase, pcnt);
+  const int slots = (P + kXcd - 1) / kXcd * nsp;  // this XCD's workgroups
+  if (pcnt <= 0) {
+    for (int s = t; s < slots; s += kPlanThreads) a.plan[s * kXcd + x] = make_int4(-1, -1, -1, 0);
+    return true;
+  }
+  const int h_lo = pbase / pairs, nh = (pbase + pcnt - 1) / pairs - h_lo + 1;
+  const int nr = nh * N;
+  const int umax = max(pcnt, min(kCusPerXcd, pcnt * nsp));
+  if (2 * nr + 4 * pcnt + 3 * umax + 4 > kPlanLdsInts) return false;
+  const int ncur = a.include_current ? N : 0;
+  int* lens_s = sh;                 // [nr]
+  int* row_of = lens_s + nr;        // [nr]: row of rank k in its head
+  int* pr_a = row_of + nr;          // [pcnt] longer row of the pair
+  int* pr_b = pr_a + pcnt;          // [pcnt] other row or -1
+  int* cost_s = pr_b + pcnt;        // [pcnt]
+  int* nu_s = cost_s + pcnt;        // [pcnt] ranges of the pair
+  int* u_pair = nu_s + pcnt;        // [umax] unit -> pair
+  int* u_rng = u_pair + umax;       // [umax] unit -> range
+  int* u_size = u_rng + umax;       // [umax] unit -> tiles of its longer range
+  int* nunits = u_size + umax;      // [1]
+  for (int e = t; e < nr; e += kPlanThreads) {
+    const int h = h_lo + e / N, r = e % N;
+    lens_s[e] = a.M == 0 ? 0 : min(max(a.route_len[static_cast<int64_t>(h) * a.route_head_rows + r], 0), a.L);
+  }
+  __syncthreads();
+  for (int e = t; e < nr; e += kPlanThreads) {
+    const int hb = e - e % N, me = e - hb, v = lens_s[e];
+    int rank = 0;
+    for (int o = 0; o < N; ++o) rank += (lens_s[hb + o] > v) || (lens_s[hb + o] == v && o < me);
+    row_of[hb + rank] = me;
+  }
+  __syncthreads();
+  for (int w = t; w < pcnt; w += kPlanThreads) {
+    const int hp = pbase + w, hb = (hp / pairs - h_lo) * N, pr = hp % pairs;
+    const int ra = row_of[hb + 2 * pr];
+    pr_a[w] = ra;
+    pr_b[w] = 2 * pr + 1 < N ? row_of[hb + 2 * pr + 1] : -1;
+    cost_s[w] = lens_s[hb + ra] + ncur;
+  }
+  __syncthreads();
+  if (t == 0) {
+    // smallest tau in [1, max cost] whose range count fits umax
+    int cmax = 1;
+    for (int w = 0; w < pcnt; ++w) cmax = max(cmax, cost_s[w]);
+    auto count = [&](int tau) {
+      int n = 0;
+      for (int w = 0; w < pcnt; ++w) n += min(max((cost_s[w] + tau - 1) / tau, 1), nsp);
+      return n;
+    };
+    int lo = 1, hi = cmax;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (count(mid) <= umax) hi = mid; else lo = mid + 1;
+    }
+    int n = 0;
+    for (int w = 0; w < pcnt; ++w) {
+      const int nu = min(max((cost_s[w] + lo - 1) / lo, 1), nsp);
+      nu_s[w] = nu;
+      for (int r = 0; r < nu; ++r) {
+        u_pair[n] = w;
+        u_rng[n] = r;
+        u_size[n] = (cost_s[w] + nu - 1) / nu;
+        ++n;
+      }
+    }
+    nunits[0] = n;
+  }
+  __syncthreads();
+  const int n = nunits[0];
+  // unit of dispatch rank `slot`: sizes descending, ties by unit index
+  for (int u = t; u < n; u += kPlanThreads) {
+    const int su = u_size[u];
+    int slot = 0;
+    for (int o = 0; o < n; ++o) slot += (u_size[o] > su) || (u_size[o] == su && o < u);
+    const int w = u_pair[u];
+    a.plan[slot * kXcd + x] = make_int4((pbase + w) / pairs, pr_a[w], pr_b[w], u_rng[u] | (nu_s[w] << 8));
+  }
+  for (int s = n + t; s < slots; s += kPlanThreads) a.plan[s * kXcd + x] = make_int4(-1, -1, -1, 0);
+  // (max, sum) = (-inf, 0) for the ranges a pair leaves unused
+  const int64_t rows = static_cast<int64_t>(a.H) * N * kBlock;
+  for (int w = 0; w < pcnt; ++w) {
+    const int nu = nu_s[w];
+    if (nu >= nsp) continue;
+    const int h = (pbase + w) / pairs;
+    for (int e = t; e < 2 * kBlock * (nsp - nu); e += kPlanThreads) {
+      const int q = e % kBlock, side = (e / kBlock) & 1, r = nu + e / (2 * kBlock);
+      const int row = side ? pr_b[w] : pr_a[w];
+      if (row < 0) continue;
+      const int64_t idx = static_cast<int64_t>(r) * rows + (static_cast<int64_t>(h) * N + row) * kBlock + q;
+      a.part_ml[idx * 2] = -INFINITY;
+      a.part_ml[idx * 2 + 1] = 0.f;
+    }
+  }
+  return true;
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int sh[kPlanLdsInts];
   const int t = threadIdx.x, x = blockIdx.x;
   const int N = a.N, pairs = (N + 1) / 2, nsp = max(a.n_split, 1);
+  if (nsp > 1 && a.part_ml && plan_split_adaptive(a, x, sh)) return;
   const int G = a.H * pairs * nsp;
   int base, cnt;
   xcd_range(x, G, base, cnt);
+  if (nsp > 1) {  // the launch has ceil(pairs / 8) * nsp slots per XCD
+    const int slots = (a.H * pairs + kXcd - 1) / kXcd * nsp;
+    for (int s = max(cnt, 0) + t; s < slots; s += kPlanThreads) a.plan[s * kXcd + x] = make_int4(-1, -1, -1, 0);
+  }
   if (cnt <= 0) return;
   const int h_lo = base / nsp / pairs, nh = (base + cnt - 1) / nsp / pairs - h_lo + 1;
   const int nr = nh * N;
@@ -1051,7 +1171,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int hb = (h - h_lo) * N;
       const int ra = row_of[hb + 2 * pr];
       const int rb = 2 * pr + 1 < N ? row_of[hb + 2 * pr + 1] : -1;
-      a.plan[slot * kXcd + x] = make_int4(h, ra, rb, id % nsp);
+      a.plan[slot * kXcd + x] = make_int4(h, ra, rb, (id % nsp) | (nsp << 8));
     }
   } else {
     for (int w = t; w < cnt; w += kPlanThreads) {
@@ -1067,7 +1187,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         if (rank == 2 * pr) ra = r;
         if (rank == 2 * pr + 1) rb = r;
       }
-      a.plan[w * kXcd + x] = make_int4(h, ra, rb, id % nsp);
+      a.plan[w * kXcd + x] = make_int4(h, ra, rb, (id % nsp) | (nsp << 8));
     }
   }
 }
@@ -1202,13 +1322,16 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
     if (!kRouted) run.plan = nullptr;
     if (kRouted && run.plan) {
       pp::PlanArgs pa{args.route_len, args.route_head_rows, args.G / args.N, args.N, args.M,
-                      args.L, args.include_current, nsp, const_cast<int4*>(run.plan)};
+                      args.L, args.include_current, nsp, const_cast<int4*>(run.plan),
+                      nsp > 1 ? args.part_ml : nullptr};
       hipLaunchKernelGGL(pp::plan_kernel, dim3(kXcd), dim3(pp::kPlanThreads), 0, stream, pa);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((pp::attn_kernel<kRouted>), dim3((args.G / args.N) * pairs * nsp),
-                       dim3(pp::kThreads), 0, stream, run);
+    // with a plan, split rows get ceil(pairs / 8) * nsp slots on every XCD
+    const int units = (args.G / args.N) * pairs;
+    const int grid = kRouted && run.plan && nsp > 1 ? kXcd * ((units + kXcd - 1) / kXcd) * nsp : units * nsp;
+    hipLaunchKernelGGL((pp::attn_kernel<kRouted>), dim3(grid), dim3(pp::kThreads), 0, stream, run);
     if (nsp > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1232,7 +1355,9 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
 
 size_t attn_plan_bytes(int H, int N, int n_split) {
   if (H < 1 || N < 1) return 0;
-  const size_t units = static_cast<size_t>(H) * ((N + 1) / 2) * (n_split > 1 ? n_split : 1);
+  const size_t pairs = static_cast<size_t>(H) * ((N + 1) / 2);
+  // split rows: every XCD gets ceil(pairs / 8) * n_split slots
+  const size_t units = n_split > 1 ? kXcd * ((pairs + kXcd - 1) / kXcd) * n_split : pairs;
   return units * sizeof(int4);
 }
 

@@ -277,12 +277,16 @@ velox_status_t velox_dense_attn(const void* q, const void* k, const void* v,
  * same attention as velox_sparse_attn / velox_dense_attn ([digest] Core
  * method, eq. 15); the difference is only the work distribution. The tile list
  * of every query row (current chunk, then the routed tiles) is cut into
- * n_split consecutive ranges, each handled by its own workgroup; the ranges'
+ * consecutive ranges, each handled by its own workgroup; the ranges'
  * unnormalised outputs and softmax (max, sum) go to the workspace and a second
- * kernel merges them (softmax is associative under rescaling). Meant for
- * shapes with few rows per GPU, e.g. one GPU's share of the heads (5 heads x 36
- * query blocks = 180 rows for 256 CUs). Results equal the unsplit call's up to
- * float rounding.
+ * kernel merges them (softmax is associative under rescaling). The dense call
+ * cuts every row into n_split ranges. The sparse call cuts each pair of rows
+ * that share a workgroup into at most n_split ranges, as many as the pairs of
+ * an XCD need to fill one round of its 32 CUs with ranges of about equal
+ * length (decided on the device from route_len, in the unit schedule); when an
+ * XCD has more pairs than CUs nothing is cut. Meant for shapes with few rows
+ * per GPU, e.g. one GPU's share of the heads (5 heads x 36 query blocks = 180
+ * rows for 256 CUs). Results equal the unsplit call's up to float rounding.
  *   n_split          1 .. VELOX_MAX_SPLIT; 1 is the unsplit call
  *   workspace        device buffer, 16-byte aligned, of at least
  *                    velox_attn_split_workspace_size(H, N, n_split) bytes

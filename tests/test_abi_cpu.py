@@ -133,7 +133,9 @@ def test_split_attention_validation(lib):
     s = ctypes.c_float(0.125)
     A = 0x10000  # aligned fake pointer
     need = lib.velox_attn_split_workspace_size(H, N, 3)
-    assert need == 3 * H * N * 128 * 130 * 4 + 3 * H * ((N + 1) // 2) * 16
+    # partial outputs, then (routed calls) a unit plan of ceil(pairs / 8) * n_split
+    # slots on each of the 8 XCDs
+    assert need == 3 * H * N * 128 * 130 * 4 + 8 * ((H * ((N + 1) // 2) + 7) // 8) * 3 * 16
     assert lib.velox_sparse_attn_workspace_size(H, N, 16, d) == H * ((N + 1) // 2) * 16
     assert lib.velox_sparse_attn_workspace_size(H, 5, 16, d) == H * 3 * 16
     assert lib.velox_sparse_attn_workspace_size(0, N, 16, d) == 0

@@ -73,3 +73,23 @@ def test_fp32_runs_unsplit():
     o_s, lse_s = velox.sparse_attn(q, k, v, r["ids"], r["lens"], wl.M, want_lse=True, n_split=4)
     torch.cuda.synchronize()
     assert torch.equal(o_s, r["o"]) and torch.equal(lse_s, r["lse"])
+
+
+@pytest.mark.parametrize("heads,n_split", [(40, 4), (5, 16)])
+def test_adaptive_ranges_match_unsplit(heads, n_split):
+    """The unit plan cuts each pair into as many ranges as one round of an
+    XCD's CUs holds (none at 40 heads: 90 pairs per XCD; up to n_split at 5
+    heads): outputs equal the unsplit call's up to float rounding on every row."""
+    wl = synth.chunk48(heads=heads)
+    say(f"chunk48 x {heads} heads, adaptive ranges up to {n_split}")
+    q, k, v = synth.make_qkv(wl, device=DEV)
+    r = run_path(wl, q, k, v)
+    ws = velox.split_workspace(q, n_split)
+    ws.fill_(0xFF)  # stale workspace contents must not leak into the merge
+    o_s, lse_s = velox.sparse_attn(q, k, v, r["ids"], r["lens"], wl.M, want_lse=True, n_split=n_split,
+                                   workspace=ws)
+    o_s2, lse_s2 = velox.sparse_attn(q, k, v, r["ids"], r["lens"], wl.M, want_lse=True, n_split=n_split,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    assert _close(o_s, r["o"], 8e-3) and _close(lse_s, r["lse"], 1e-4)
+    assert torch.equal(o_s, o_s2) and torch.equal(lse_s, lse_s2)
