@@ -123,3 +123,28 @@ def test_unit_plan_matches_in_kernel_ranking_bitwise(wlname, N):
     assert torch.equal(o1, o0) and torch.equal(l1, l0)
     o2, l2 = velox.sparse_attn(q, k, v, ids, lens, wl.M, want_lse=True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("n_split", [2, 5, 16])
+def test_adaptive_split_odd_blocks_and_few_pairs(n_split):
+    """Split rows with few pairs per XCD (3 heads x 3 pairs: two XCDs hold two
+    pairs, six hold one), a pair whose second row does not exist (N = 5), a
+    row without routed tiles, and routes of very different lengths, so the
+    unit plan cuts pairs into different numbers of ranges: every row equals
+    the unsplit call's up to float rounding, sampled rows the oracle's."""
+    H, N, M = 3, 5, 60
+    rng = np.random.default_rng(11 + n_split)
+    lens = rng.integers(1, 55, size=(H, N))
+    lens[2, 4] = 0
+    lens[0, 0] = 55
+    q, k, v, ids, ln, routes = _case(H, N, M, lens, 20 + n_split)
+    q, k, v, ids, ln = (t.to(DEV) for t in (q, k, v, ids, ln))
+    say(f"adaptive split: H={H} N={N} M={M} n_split={n_split}")
+    o, lse = velox.sparse_attn(q, k, v, ids, ln, M, want_lse=True)
+    ws = velox.split_workspace(q, n_split)
+    ws.fill_(0xFF)
+    o_s, lse_s = velox.sparse_attn(q, k, v, ids, ln, M, want_lse=True, n_split=n_split, workspace=ws)
+    torch.cuda.synchronize()
+    assert float((o_s.float() - o.float()).abs().max()) <= 8e-3
+    assert float((lse_s - lse).abs().max()) <= 1e-4
+    _check(q, k, v, o_s, lse_s, routes, [(0, 0), (1, 4), (2, 4), (2, 1)], M, N, True)
