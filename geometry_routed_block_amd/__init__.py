@@ -306,9 +306,10 @@ def sparse_attn(q, k, v, route_ids, route_len, M: int, include_current: bool = T
 
     route_ids [H][N][L] / route_len [H][N] give one route per head; [N][L] / [N]
     (or [1][N][L] / [1][N]) one route per query block shared by all heads.
-    n_split > 1 cuts every row's tiles into that many ranges (per-head routes
-    only); `workspace` is then a device buffer of split_workspace(q, n_split)'s
-    size (allocated here when None). With per-head routes and n_split = 1 the
+    n_split > 1 cuts rows' tiles into ranges (per-head routes only): each pair
+    of rows into at most n_split, as many as one round of an XCD's CUs holds
+    (none when an XCD has more pairs than CUs); `workspace` is then a device
+    buffer of split_workspace(q, n_split)'s size (allocated here when None). With per-head routes and n_split = 1 the
     workspace holds the call's unit schedule: attn_workspace(q, L) bytes
     (allocated here when None).
     """
