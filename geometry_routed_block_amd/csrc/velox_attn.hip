@@ -1194,47 +1194,91 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 }  // namespace pp
 
-// Combines the n_split ranges of every query row (four threads per row, 32
+// Combines the n_split ranges of every query row (eight threads per row, 16
 // dims each): m = max m_s, l = sum of 2^(m_s - m) l_s, O = sum of
 // 2^(m_s - m) O_s / l, lse = m ln 2 + ln l; a row without any tile gets O = 0
-// and lse = -inf. rows = H * N * 128, in the layout of o and lse.
+// and lse = -inf. rows = H * N * 128, in the layout of o and lse. The maxima of
+// all ranges and the partial outputs of the first four are requested together;
+// further ranges, four at a time, only up to the row's last range with tiles
+// (the ranges a unit plan leaves unused follow the used ones). Each group is
+// folded into a running maximum, weight sum and output; a range without tiles
+// (maximum -inf; its partial output was never written) is dropped by a
+// select, so its memory never enters the sums.
+constexpr int kMergeMaxSplit = 16;
 __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml, int n_split,
                                                           int64_t rows, bf16_t* __restrict__ o,
                                                           float* __restrict__ lse) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = gid >> 2;
-  const int quarter = static_cast<int>(gid & 3);
+  const int64_t row = gid >> 3;
+  const int eighth = static_cast<int>(gid & 7);
   if (row >= rows) return;
-  float m = -INFINITY;
-  for (int s = 0; s < n_split; ++s) m = fmaxf(m, part_ml[(s * rows + row) * 2]);
-  float l = 0.f, acc[32];
+  auto range_row = [&](int s) { return static_cast<int64_t>(min(s, n_split - 1)) * rows + row; };
+  float2 ml[kMergeMaxSplit];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = part_ml[(s * rows + row) * 2];
-      if (ms == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - m);
-      l += w * part_ml[(s * rows + row) * 2 + 1];
-      const float4* src = reinterpret_cast<const float4*>(part_o + (s * rows + row) * 128 + quarter * 32);
+  for (int s = 0; s < kMergeMaxSplit; ++s) ml[s] = *reinterpret_cast<const float2*>(part_ml + range_row(s) * 2);
+  float4 x[4][4];
+  auto load_group = [&](int s0) {
 #pragma unroll
-      for (int e4 = 0; e4 < 8; ++e4) {
-        const float4 x = src[e4];
-        acc[4 * e4 + 0] += w * x.x;
-        acc[4 * e4 + 1] += w * x.y;
-        acc[4 * e4 + 2] += w * x.z;
-        acc[4 * e4 + 3] += w * x.w;
+    for (int u = 0; u < 4; ++u) {
+      const float4* src = reinterpret_cast<const float4*>(part_o + range_row(s0 + u) * 128 + eighth * 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[u][c] = src[c];
+    }
+  };
+  load_group(0);
+  int n_used = 0;
+#pragma unroll
+  for (int s = 0; s < kMergeMaxSplit; ++s)
+    if (s < n_split && ml[s].x != -INFINITY) n_used = s + 1;
+  float m = -INFINITY, l = 0.f, acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  auto fold = [&](int s0) {
+    bool use[4];
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      use[u] = s0 + u < n_used && ml[s0 + u].x != -INFINITY;
+      if (use[u]) mc = fmaxf(mc, ml[s0 + u].x);
+    }
+    if (mc == -INFINITY) return;  // no tile in this row so far
+    const float a = __builtin_amdgcn_exp2f(m - mc);  // 0 while m is -inf
+    l *= a;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] *= a;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = use[u] ? __builtin_amdgcn_exp2f(ml[s0 + u].x - mc) : 0.f;
+      l += use[u] ? w * ml[s0 + u].y : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[4 * c + 0] += use[u] ? w * x[u][c].x : 0.f;
+        acc[4 * c + 1] += use[u] ? w * x[u][c].y : 0.f;
+        acc[4 * c + 2] += use[u] ? w * x[u][c].z : 0.f;
+        acc[4 * c + 3] += use[u] ? w * x[u][c].w : 0.f;
       }
+    }
+    m = mc;
+  };
+  fold(0);
+#pragma unroll
+  for (int s0 = 4; s0 < kMergeMaxSplit; s0 += 4) {
+    if (s0 < n_used) {
+      load_group(s0);
+      fold(s0);
     }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(o + row * 128 + quarter * 32);
+  uint32_t w[8];
 #pragma unroll
-  for (int e2 = 0; e2 < 16; ++e2)
-    dst[e2] = static_cast<uint32_t>(f32_to_bf16(acc[2 * e2] * inv)) |
-              (static_cast<uint32_t>(f32_to_bf16(acc[2 * e2 + 1] * inv)) << 16);
-  if (lse && quarter == 0) lse[row] = l > 0.f ? m * 0.6931471805599453f + logf(l) : -INFINITY;
+  for (int e2 = 0; e2 < 8; ++e2)
+    w[e2] = static_cast<uint32_t>(f32_to_bf16(acc[2 * e2] * inv)) |
+            (static_cast<uint32_t>(f32_to_bf16(acc[2 * e2 + 1] * inv)) << 16);
+  uint4* dst = reinterpret_cast<uint4*>(o + row * 128 + eighth * 16);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  if (lse && eighth == 0) lse[row] = l > 0.f ? m * 0.6931471805599453f + logf(l) : -INFINITY;
 }
 
 // ---------------------------------------------------------------- fp32
@@ -1336,7 +1380,7 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t rows = static_cast<int64_t>(args.G) * kBlock;
-      hipLaunchKernelGGL(split_merge_kernel, dim3(static_cast<unsigned>((rows * 4 + 255) / 256)), dim3(256), 0,
+      hipLaunchKernelGGL(split_merge_kernel, dim3(static_cast<unsigned>((rows * 8 + 255) / 256)), dim3(256), 0,
                          stream, args.part_o, args.part_ml, nsp, rows, static_cast<bf16_t*>(args.o), args.lse);
     }
     return hipGetLastError();
