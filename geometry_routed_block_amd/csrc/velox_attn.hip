@@ -66,8 +66,8 @@ struct AttnArgs {
   int n_split;
   float* part_o;
   float* part_ml;
-  // Unit schedule of the routed d = 128 bf16 kernel written by plan_kernel
-  // (nullptr: every workgroup ranks the units itself): entry b is the unit of
+  // Unit schedule of the routed d = 128 bf16 kernel written by plan_kernel or
+  // plan_split_kernel (nullptr: every workgroup ranks the units itself): entry b is the unit of
   // workgroup b, {head, longer row, shorter row or -1, range}.
   const int4* plan;
 };
@@ -985,8 +985,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- unit schedule
 //
-// plan_kernel writes the schedule of the routed kernel once per call, so that
-// no attention workgroup spends its start ranking units. One workgroup per
+// plan_kernel (plan_split_kernel for split rows) writes the schedule of the
+// routed kernel once per call, so that no attention workgroup spends its start
+// ranking units. One workgroup per
 // XCD: its contiguous range of (head, pair, range) ids (xcd_range), where a
 // pair is ranks 2 pr and 2 pr + 1 of the head's rows ordered by route length
 // (longest first, ties by row), and a unit's cost is its longer row's tile
@@ -1007,6 +1008,22 @@ struct PlanArgs {
 constexpr int kPlanThreads = 512;
 constexpr int kPlanLdsInts = 12288;
 constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs in 8 XCDs
+
+// Rank of value vme at index me among vals[0, n): the count of larger values
+// and of equal ones at lower indices (descending order, ties by index). The
+// LDS reads go out eight at a time, with one wait per eight.
+__device__ __forceinline__ int rank_desc(const int* vals, int n, int me, int vme) {
+  int rank = 0, o = 0;
+  for (; o + 8 <= n; o += 8) {
+    int x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = vals[o + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rank += (x[u] > vme) || (x[u] == vme && o + u < me);
+  }
+  for (; o < n; ++o) rank += (vals[o] > vme) || (vals[o] == vme && o < me);
+  return rank;
+}
 
 // Split rows with a plan: each XCD owns a contiguous range of (head, pair)
 // ids. A pair whose cost (its longer row's tiles) is c is cut into
@@ -1031,7 +1048,7 @@ __device__ bool plan_split_adaptive(const PlanArgs& a, int x, int* sh) {
   const int h_lo = pbase / pairs, nh = (pbase + pcnt - 1) / pairs - h_lo + 1;
   const int nr = nh * N;
   const int umax = max(pcnt, min(kCusPerXcd, pcnt * nsp));
-  if (2 * nr + 4 * pcnt + 3 * umax + 4 > kPlanLdsInts) return false;
+  if (2 * nr + 4 * pcnt + 3 * umax + 6 > kPlanLdsInts) return false;
   const int ncur = a.include_current ? N : 0;
   int* lens_s = sh;                 // [nr]
   int* row_of = lens_s + nr;        // [nr]: row of rank k in its head
@@ -1043,16 +1060,20 @@ __device__ bool plan_split_adaptive(const PlanArgs& a, int x, int* sh) {
   int* u_rng = u_pair + umax;       // [umax] unit -> range
   int* u_size = u_rng + umax;       // [umax] unit -> tiles of its longer range
   int* nunits = u_size + umax;      // [1]
+  int* red = nunits + 1;            // [2]: largest cost, smallest fitting tau
   for (int e = t; e < nr; e += kPlanThreads) {
     const int h = h_lo + e / N, r = e % N;
     lens_s[e] = a.M == 0 ? 0 : min(max(a.route_len[static_cast<int64_t>(h) * a.route_head_rows + r], 0), a.L);
   }
   __syncthreads();
   for (int e = t; e < nr; e += kPlanThreads) {
-    const int hb = e - e % N, me = e - hb, v = lens_s[e];
-    int rank = 0;
-    for (int o = 0; o < N; ++o) rank += (lens_s[hb + o] > v) || (lens_s[hb + o] == v && o < me);
-    row_of[hb + rank] = me;
+    const int hb = e - e % N, me = e - hb;
+    row_of[hb + rank_desc(lens_s + hb, N, me, lens_s[e])] = me;
+  }
+  __syncthreads();
+  if (t == 0) {
+    red[0] = 1;
+    red[1] = 0x7fffffff;
   }
   __syncthreads();
   for (int w = t; w < pcnt; w += kPlanThreads) {
@@ -1061,69 +1082,90 @@ __device__ bool plan_split_adaptive(const PlanArgs& a, int x, int* sh) {
     pr_a[w] = ra;
     pr_b[w] = 2 * pr + 1 < N ? row_of[hb + 2 * pr + 1] : -1;
     cost_s[w] = lens_s[hb + ra] + ncur;
+    atomicMax(&red[0], cost_s[w]);
   }
   __syncthreads();
-  if (t == 0) {
-    // smallest tau in [1, max cost] whose range count fits umax
-    int cmax = 1;
-    for (int w = 0; w < pcnt; ++w) cmax = max(cmax, cost_s[w]);
-    auto count = [&](int tau) {
-      int n = 0;
-      for (int w = 0; w < pcnt; ++w) n += min(max((cost_s[w] + tau - 1) / tau, 1), nsp);
-      return n;
-    };
-    int lo = 1, hi = cmax;
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if (count(mid) <= umax) hi = mid; else lo = mid + 1;
-    }
-    int n = 0;
-    for (int w = 0; w < pcnt; ++w) {
-      const int nu = min(max((cost_s[w] + lo - 1) / lo, 1), nsp);
-      nu_s[w] = nu;
-      for (int r = 0; r < nu; ++r) {
-        u_pair[n] = w;
-        u_rng[n] = r;
-        u_size[n] = (cost_s[w] + nu - 1) / nu;
-        ++n;
+  // ranges of a pair of cost c for a given tau: min(max(ceil(c / tau), 1),
+  // n_split), i.e. one plus the number of k in [1, n_split) with c > k tau
+  auto ranges_of = [nsp](int c, int tau) {
+    int nu = 1;
+    for (int k = 1; k < nsp; ++k) nu += c > k * tau;
+    return nu;
+  };
+  // the smallest tau in [1, largest cost] whose range count fits umax (the
+  // largest cost always does: one range per pair), every tau counted by its
+  // own thread
+  {
+    const int cmax = red[0];
+    for (int tau = 1 + t; tau <= cmax; tau += kPlanThreads) {
+      int cnt = 0, w = 0;
+      for (; w + 8 <= pcnt; w += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cost_s[w + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cnt += ranges_of(c[u], tau);
+      }
+      for (; w < pcnt; ++w) cnt += ranges_of(cost_s[w], tau);
+      if (cnt <= umax) {
+        atomicMin(&red[1], tau);
+        break;  // larger taus of this thread fit too
       }
     }
-    nunits[0] = n;
+  }
+  __syncthreads();
+  const int lo = red[1];
+  for (int w = t; w < pcnt; w += kPlanThreads) nu_s[w] = ranges_of(cost_s[w], lo);
+  __syncthreads();
+  // units in pair order: pair w's ranges start after those of pairs 0 .. w-1
+  for (int w = t; w < pcnt; w += kPlanThreads) {
+    int first = 0, o = 0;
+    for (; o + 8 <= w; o += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = nu_s[o + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) first += c[u];
+    }
+    for (; o < w; ++o) first += nu_s[o];
+    const int nu = nu_s[w], size = (cost_s[w] + nu - 1) / nu;
+    for (int r = 0; r < nu; ++r) {
+      u_pair[first + r] = w;
+      u_rng[first + r] = r;
+      u_size[first + r] = size;
+    }
+    if (w == pcnt - 1) nunits[0] = first + nu;
   }
   __syncthreads();
   const int n = nunits[0];
   // unit of dispatch rank `slot`: sizes descending, ties by unit index
   for (int u = t; u < n; u += kPlanThreads) {
-    const int su = u_size[u];
-    int slot = 0;
-    for (int o = 0; o < n; ++o) slot += (u_size[o] > su) || (u_size[o] == su && o < u);
+    const int slot = rank_desc(u_size, n, u, u_size[u]);
     const int w = u_pair[u];
     a.plan[slot * kXcd + x] = make_int4((pbase + w) / pairs, pr_a[w], pr_b[w], u_rng[u] | (nu_s[w] << 8));
   }
   for (int s = n + t; s < slots; s += kPlanThreads) a.plan[s * kXcd + x] = make_int4(-1, -1, -1, 0);
-  // (max, sum) = (-inf, 0) for the ranges a pair leaves unused
+  // (max, sum) = (-inf, 0) for the ranges a pair leaves unused: one wave per
+  // (pair, range, row) triple writes the 128 queries' pairs (1 KiB, 16 bytes
+  // per lane)
   const int64_t rows = static_cast<int64_t>(a.H) * N * kBlock;
-  for (int w = 0; w < pcnt; ++w) {
-    const int nu = nu_s[w];
-    if (nu >= nsp) continue;
+  const int lane = t % kWave, wave = t / kWave;
+  for (int tr = wave; tr < pcnt * nsp * 2; tr += kPlanThreads / kWave) {
+    const int w = tr / (2 * nsp), r = (tr >> 1) % nsp, side = tr & 1;
+    const int row = side ? pr_b[w] : pr_a[w];
+    if (r < nu_s[w] || row < 0) continue;
     const int h = (pbase + w) / pairs;
-    for (int e = t; e < 2 * kBlock * (nsp - nu); e += kPlanThreads) {
-      const int q = e % kBlock, side = (e / kBlock) & 1, r = nu + e / (2 * kBlock);
-      const int row = side ? pr_b[w] : pr_a[w];
-      if (row < 0) continue;
-      const int64_t idx = static_cast<int64_t>(r) * rows + (static_cast<int64_t>(h) * N + row) * kBlock + q;
-      a.part_ml[idx * 2] = -INFINITY;
-      a.part_ml[idx * 2 + 1] = 0.f;
-    }
+    const int64_t idx = static_cast<int64_t>(r) * rows + (static_cast<int64_t>(h) * N + row) * kBlock + 2 * lane;
+    *reinterpret_cast<float4*>(a.part_ml + idx * 2) = make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
   }
   return true;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int sh[kPlanLdsInts];
-  const int t = threadIdx.x, x = blockIdx.x;
+// Units of equal ranges (every pair cut into n_split ranges, or none), the
+// XCD's share of them longest first.
+__device__ void plan_uniform(const PlanArgs& a, int x, int* sh) {
+  const int t = threadIdx.x;
   const int N = a.N, pairs = (N + 1) / 2, nsp = max(a.n_split, 1);
-  if (nsp > 1 && a.part_ml && plan_split_adaptive(a, x, sh)) return;
   const int G = a.H * pairs * nsp;
   int base, cnt;
   xcd_range(x, G, base, cnt);
@@ -1190,6 +1232,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       a.plan[w * kXcd + x] = make_int4(h, ra, rb, (id % nsp) | (nsp << 8));
     }
   }
+}
+
+// One workgroup per XCD writes that XCD's units: plan_kernel for unsplit
+// rows, plan_split_kernel for split rows (adaptive ranges, or equal ranges
+// when the XCD's rows do not fit in LDS).
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int sh[kPlanLdsInts];
+  plan_uniform(a, blockIdx.x, sh);
+}
+__global__ __launch_bounds__(kPlanThreads) void plan_split_kernel(PlanArgs a) {
+  __shared__ int sh[kPlanLdsInts];
+  if (!(a.part_ml && plan_split_adaptive(a, blockIdx.x, sh))) plan_uniform(a, blockIdx.x, sh);
 }
 
 }  // namespace pp
@@ -1368,7 +1422,10 @@ static hipError_t launch_one(const AttnArgs& args, bool bf16, hipStream_t stream
       pp::PlanArgs pa{args.route_len, args.route_head_rows, args.G / args.N, args.N, args.M,
                       args.L, args.include_current, nsp, const_cast<int4*>(run.plan),
                       nsp > 1 ? args.part_ml : nullptr};
-      hipLaunchKernelGGL(pp::plan_kernel, dim3(kXcd), dim3(pp::kPlanThreads), 0, stream, pa);
+      if (nsp > 1)
+        hipLaunchKernelGGL(pp::plan_split_kernel, dim3(kXcd), dim3(pp::kPlanThreads), 0, stream, pa);
+      else
+        hipLaunchKernelGGL(pp::plan_kernel, dim3(kXcd), dim3(pp::kPlanThreads), 0, stream, pa);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
