@@ -247,6 +247,9 @@ size_t velox_sparse_attn_workspace_size(int H, int N, int L, int d) {
   return velox::attn_plan_bytes(H, N, 1);
 }
 
+// split_merge_kernel folds at most 16 ranges per row (kMergeMaxSplit)
+static_assert(VELOX_MAX_SPLIT <= 16, "the split-row merge reads at most 16 ranges per row");
+
 // Split settings into the launch config: the workspace holds part_o
 // [n_split][rows][128], then part_ml [n_split][rows][2], then the unit plan.
 static velox_status_t set_split(velox::AttnConfig& c, int n_split, void* workspace,
