@@ -75,11 +75,13 @@ def test_fp32_runs_unsplit():
     assert torch.equal(o_s, r["o"]) and torch.equal(lse_s, r["lse"])
 
 
-@pytest.mark.parametrize("heads,n_split", [(40, 4), (5, 16)])
+@pytest.mark.parametrize("heads,n_split", [(40, 4), (40, 16), (5, 16)])
 def test_adaptive_ranges_match_unsplit(heads, n_split):
     """The unit plan cuts each pair into as many ranges as one round of an
-    XCD's CUs holds (none at 40 heads: 90 pairs per XCD; up to n_split at 5
-    heads): outputs equal the unsplit call's up to float rounding on every row."""
+    XCD's CUs holds (none at 40 heads: 90 pairs per XCD, so every row has
+    n_split - 1 unused ranges whose partials are the 0xFF fill; up to n_split
+    at 5 heads): outputs equal the unsplit call's up to float rounding on
+    every row."""
     wl = synth.chunk48(heads=heads)
     say(f"chunk48 x {heads} heads, adaptive ranges up to {n_split}")
     q, k, v = synth.make_qkv(wl, device=DEV)
