@@ -22,7 +22,7 @@ def _close(a, b, atol):
     return float((a.float() - b.float()).abs().max()) <= atol
 
 
-@pytest.mark.parametrize("n_split", [2, 3, 7])
+@pytest.mark.parametrize("n_split", [2, 3, 7, 16])
 def test_split_at_five_heads_of_chunk48(n_split):
     wl = synth.chunk48(heads=5)
     say(f"chunk48 x 5 heads, n_split={n_split}")
