@@ -89,6 +89,12 @@ def block_mean(x, nblk: int | None = None, out=None):
     return out
 
 
+def _kbar_rows(kbar, H, M, d):
+    """kbar must hold M key means of q's head dim for each of q's heads."""
+    if kbar.dim() != 3 or kbar.shape[0] != H or kbar.shape[1] < M or kbar.shape[2] != d:
+        raise ValueError(f"kbar must be [H][>=M][d] = [{H}][>={M}][{d}] (got {tuple(kbar.shape)})")
+
+
 def route_scores(q, kbar, M: int, scale: float | None = None, out=None):
     """Block importance p [H][N][M] = softmax over history of scale * qbar . kbar."""
     torch = _torch()
@@ -97,11 +103,14 @@ def route_scores(q, kbar, M: int, scale: float | None = None, out=None):
     N = NT // VELOX_BLOCK
     if kbar.dtype != torch.float32:
         raise TypeError("kbar must be float32")
+    _kbar_rows(kbar, H, M, d)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if out is None:
         out = torch.empty(H, N, M, dtype=torch.float32, device=q.device)
     _require_cuda(out)
     _contig(out, "p")
+    if out.dtype != torch.float32 or out.numel() != H * N * M:
+        raise ValueError(f"p must be float32 [H][N][M] = [{H}][{N}][{M}] (got {tuple(out.shape)})")
     lib = _lib.load()
     _lib.check(lib.velox_route_scores(q.data_ptr(), _dtype_code(q), _rows(q, "q"), kbar.data_ptr(),
                                       _rows(kbar, "kbar"), H, N, M, d, ctypes.c_float(scale),
@@ -120,6 +129,7 @@ def route_scores_shared(q, kbar, M: int, scale: float | None = None, logits=None
     N = NT // VELOX_BLOCK
     if kbar.dtype != torch.float32:
         raise TypeError("kbar must be float32")
+    _kbar_rows(kbar, H, M, d)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if logits is None:
         logits = torch.empty(H, N, M, dtype=torch.float32, device=q.device)

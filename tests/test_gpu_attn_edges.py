@@ -148,3 +148,22 @@ def test_adaptive_split_odd_blocks_and_few_pairs(n_split):
     assert float((o_s.float() - o.float()).abs().max()) <= 8e-3
     assert float((lse_s - lse).abs().max()) <= 1e-4
     _check(q, k, v, o_s, lse_s, routes, [(0, 0), (1, 4), (2, 4), (2, 1)], M, N, True)
+
+
+def test_binding_rejects_misshaped_router_tensors():
+    """The binding raises before any launch when kbar holds too few history
+    rows or another head count / head dim, or when p is not [H][N][M]: the C
+    ABI sees only pointers and would read or write out of bounds."""
+    H, N, M, d = 2, 3, 10, 128
+    q = torch.zeros(H, N * 128, d, dtype=torch.bfloat16, device=DEV)
+    for bad in ((H, M - 1, d), (H + 1, M, d), (H, M, 64)):
+        with pytest.raises(ValueError):
+            velox.route_scores(q, torch.zeros(*bad, device=DEV), M)
+        with pytest.raises(ValueError):
+            velox.route_scores_shared(q, torch.zeros(*bad, device=DEV), M)
+    kbar = torch.zeros(H, M, d, device=DEV)
+    with pytest.raises(ValueError):
+        velox.route_scores(q, kbar, M, out=torch.empty(H, N, M - 1, device=DEV))
+    p = velox.route_scores(q, kbar, M)
+    torch.cuda.synchronize()
+    assert torch.allclose(p, torch.full_like(p, 1.0 / M))   # zero means: uniform importance
