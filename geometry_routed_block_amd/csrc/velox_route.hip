@@ -222,7 +222,9 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   const int nq = min(QB, N - i0);
 
   // history rows of step 2: a group of kLpr lanes shares a row, each lane
-  // holding kDpl consecutive dims (d = 128: 8 lanes of 16 dims; d = 64: 8 of 8)
+  // holding kDpl dims (d = 128: 8 lanes of 16 dims; d = 64: 8 of 8) as
+  // float4 pieces kLpr float4 apart, so that each load instruction reads one
+  // whole 128-byte line of every row (dims 4 kLpr c + 4 j8 .. + 3 in piece c)
   constexpr int kDpl = D == 128 ? 16 : 8;
   constexpr int kLpr = D / kDpl, kRpw = kWave / kLpr;
   constexpr int kRowsPerIt = kRpw * (kScoreThreads / kWave);
@@ -232,10 +234,10 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   const float* kb = kbar + h * ld_kbar_h;
   auto load_row = [&](int r, float (&x)[kDpl]) {
     const float4* src =
-        reinterpret_cast<const float4*>(kb + static_cast<int64_t>(min(r, M - 1)) * D + j8 * kDpl);
+        reinterpret_cast<const float4*>(kb + static_cast<int64_t>(min(r, M - 1)) * D + j8 * 4);
 #pragma unroll
     for (int c = 0; c < kDpl / 4; ++c) {
-      const float4 u = src[c];
+      const float4 u = src[c * kLpr];
       x[4 * c] = u.x; x[4 * c + 1] = u.y; x[4 * c + 2] = u.z; x[4 * c + 3] = u.w;
     }
   };
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
   }
 
   // 2. logits. The lanes of a group share one history row: lane j8 loads its
-  // kDpl dims (a row is read contiguously by its group) and dots them with the
+  // kDpl dims (the group reads whole lines of the row) and dots them with the
   // same dims of every query mean, which it keeps in registers; DPP adds then
   // sum the group's partials (every lane ends with the row's dot products). The
   // loads of the next kBatch rows are issued before the arithmetic of the
@@ -325,12 +327,9 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int e = 0; e < kDpl; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + j8 * kDpl + e] : 0.f;
+    for (int e = 0; e < kDpl; ++e) qv[qb][e] = qb < nq ? qbar[qb * D + (e / 4) * 4 * kLpr + j8 * 4 + e % 4] : 0.f;
   float lmax = -INFINITY;  // running maximum of the logits this lane stores
-  for (int r0 = 0; r0 < M; r0 += kBatch * kRowsPerIt) {
-    float nx[kBatch][kDpl];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) load_row(r0 + (kBatch + b) * kRowsPerIt + r_me, nx[b]);
+  auto dots = [&](int r0, float (&xs)[kBatch][kDpl]) {
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int r = r0 + b * kRowsPerIt + r_me;
@@ -339,7 +338,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
       for (int qb = 0; qb < QB; ++qb) {
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < kDpl; ++e) acc = fmaf(qv[qb][e], kx[b][e], acc);
+        for (int e = 0; e < kDpl; ++e) acc = fmaf(qv[qb][e], xs[b][e], acc);
         acc = group_sum<kLpr>(acc);
         if (j8 == qb) mine = acc;
       }
@@ -348,10 +347,18 @@ __global__ __launch_bounds__(kScoreThreads) void route_scores_kernel(
         lmax = fmaxf(lmax, mine * scale);
       }
     }
+  };
+  // two row buffers used in turn (no register copies between steps)
+  constexpr int kStep = kBatch * kRowsPerIt;
+  for (int r0 = 0; r0 < M; r0 += 2 * kStep) {
+    float nx[kBatch][kDpl];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b)
+    for (int b = 0; b < kBatch; ++b) load_row(r0 + kStep + b * kRowsPerIt + r_me, nx[b]);
+    dots(r0, kx);
+    if (r0 + kStep >= M) break;
 #pragma unroll
-      for (int e = 0; e < kDpl; ++e) kx[b][e] = nx[b][e];
+    for (int b = 0; b < kBatch; ++b) load_row(r0 + 2 * kStep + b * kRowsPerIt + r_me, kx[b]);
+    dots(r0 + kStep, nx);
   }
   __syncthreads();
 
