@@ -79,10 +79,16 @@ def block_mean(x, nblk: int | None = None, out=None):
     _require_cuda(x)
     H, T, d = x.shape
     nblk = T // VELOX_BLOCK if nblk is None else nblk
+    if not 0 <= nblk <= T // VELOX_BLOCK:
+        raise ValueError(f"nblk={nblk} blocks do not fit in x's {T} token rows")
     if out is None:
         out = torch.empty(H, nblk, d, dtype=torch.float32, device=x.device)
     _require_cuda(out)
-    _rows(out.view(H, nblk, d) if out.dim() == 3 else out, "out")
+    if out.dtype != torch.float32:
+        raise TypeError("out must be float32")
+    if out.dim() == 3 and (out.shape[0] != H or out.shape[1] < nblk or out.shape[2] != d):
+        raise ValueError(f"out must be [H][>=nblk][d] = [{H}][>={nblk}][{d}] (got {tuple(out.shape)})")
+    _rows(out.view(H, nblk, d) if out.dim() != 3 else out, "out")
     lib = _lib.load()
     _lib.check(lib.velox_block_mean(x.data_ptr(), _dtype_code(x), _rows(x, "x"), H, nblk, d,
                                     out.data_ptr(), out.stride(0), _stream(x)))
@@ -469,10 +475,20 @@ def kv_append(k_new, v_new, T: int, height: int, width: int, chunk_index: int, c
         raise ValueError("cells must be int32 [height*width]")
     _contig(cells, "cells")
     H, _, d = k_new.shape
+    n_tok = T * height * width
+    if k_new.shape[1] < n_tok:
+        raise ValueError(f"k_new and v_new must hold T*height*width = {n_tok} token rows per head")
+    if (k_cache.dim() != 3 or k_cache.shape[0] != H or k_cache.shape[2] != d
+            or k_cache.shape[1] < token_offset + n_tok):
+        raise ValueError(f"k_cache and v_cache must be [H][>=token_offset+{n_tok}][d] = "
+                         f"[{H}][>={token_offset + n_tok}][{d}] (got {tuple(k_cache.shape)})")
     kb_ptr, kb_ld = 0, 0
     if kbar is not None:
         if kbar.dtype != torch.float32:
             raise ValueError("kbar must be float32")
+        nb_end = (token_offset + n_tok + VELOX_BLOCK - 1) // VELOX_BLOCK
+        if kbar.dim() != 3 or kbar.shape[0] != H or kbar.shape[2] != d or kbar.shape[1] < nb_end:
+            raise ValueError(f"kbar must be [H][>={nb_end}][d] (got {tuple(kbar.shape)})")
         kb_ptr, kb_ld = kbar.data_ptr(), _rows(kbar, "kbar")
     lib = _lib.load()
     _lib.check(lib.velox_kv_append(k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new),

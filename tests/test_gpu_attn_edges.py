@@ -167,3 +167,32 @@ def test_binding_rejects_misshaped_router_tensors():
     p = velox.route_scores(q, kbar, M)
     torch.cuda.synchronize()
     assert torch.allclose(p, torch.full_like(p, 1.0 / M))   # zero means: uniform importance
+
+
+def test_binding_rejects_misshaped_block_mean_and_append_tensors():
+    """block_mean: more blocks than x holds, or an output with too few rows;
+    kv_append: a cache too short for the chunk at its offset, another head
+    count, or a key-mean cache too short: all raise before any launch."""
+    H, d = 2, 128
+    x = torch.zeros(H, 4 * 128, d, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        velox.block_mean(x, nblk=5)
+    with pytest.raises(ValueError):
+        velox.block_mean(x, out=torch.empty(H, 3, d, device=DEV))
+    T, Hl, Wl = 1, 16, 16                       # 256 tokens = 2 blocks
+    new = torch.zeros(H, T * Hl * Wl, d, dtype=torch.bfloat16, device=DEV)
+    cells = torch.from_numpy(velox.gilbert_curve(Wl, Hl)).to(DEV)
+    short = torch.zeros(H, 3 * 128, d, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):             # offset 256 + 256 tokens > 384 rows
+        velox.kv_append(new, new, T, Hl, Wl, 0, cells, short, short, 256)
+    other = torch.zeros(H + 1, 4 * 128, d, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        velox.kv_append(new, new, T, Hl, Wl, 0, cells, other, other, 0)
+    cache = torch.zeros(H, 4 * 128, d, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        velox.kv_append(new, new, T, Hl, Wl, 0, cells, cache, cache.clone(), 256,
+                        kbar=torch.zeros(H, 3, d, device=DEV))
+    kb = torch.zeros(H, 4, d, device=DEV)
+    velox.kv_append(new, new, T, Hl, Wl, 0, cells, cache, cache.clone(), 256, kbar=kb)
+    torch.cuda.synchronize()
+    assert float(kb.abs().max()) == 0.0         # zero chunk: zero key means
