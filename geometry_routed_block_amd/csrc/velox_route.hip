@@ -166,11 +166,13 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const T* __restrict__ x
 //     per lane, across the row groups of a wave by lane swaps, then across
 //     waves in LDS. The first history rows of step 2 are requested before that
 //     reduction, so their latency overlaps it.
-//  2. logits: a group of D / 8 lanes shares each history row (contiguous
-//     16-byte loads of kbar[h][r], several rows in flight); each lane dots its
-//     8 dims with the QB query means held in registers and DPP adds sum the
+//  2. logits: a group of 8 lanes shares each history row (each 16-byte load
+//     instruction reads whole 128-byte lines of kbar[h][r], the next rows in
+//     flight while the current ones are summed); each lane dots its D / 8
+//     dims with the QB query means held in registers and DPP adds sum the
 //     group. Logits of the QB rows stay in LDS; each lane keeps the running
-//     maximum of the logits it wrote.
+//     maximum of the logits it wrote. (With M >= D the query means of step 1
+//     come from a block-mean launch instead, read back from the output rows.)
 //  3. softmax over the history blocks of each row (all QB rows reduced
 //     together), written coalesced: exp through the hardware exp2 and one
 //     reciprocal per row (within a few float32 ulps of the correctly rounded
